@@ -1,0 +1,162 @@
+/*
+ * spava.h -- C ABI of the Spava / APB-V approximate-attention prefill library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2601.21444; pages: "Spava: Accelerating Long-Video Understanding
+ * via Sequence-Parallelism-aware Approximate Attention", abstract; and the
+ * explainer "APB-V: ..." on gist.science, section "Methodik: APB-V" >
+ * "Approximativer Attention-Mechanismus"): the token sequence is cut into H
+ * contiguous context blocks. Queries of block h attend causally to their own keys,
+ * to an anchor block (the first A tokens) and to the passing blocks of all earlier
+ * blocks: the l most important key/value rows each earlier block forwards, chosen
+ * by query-to-context attention scores. Here all H "hosts" run on one GPU.
+ *
+ * Two calls make one prefill layer:
+ *   spava_select_passing   scores every key of blocks 0..H-2 and picks each
+ *                          block's passing rows per KV head;
+ *   spava_approx_attn_fwd  gathers anchor + passing rows and runs the attention.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     allocates no device memory: scratch space is the caller's `workspace`, sized
+ *     by the matching *_workspace_bytes query. Nothing is retained after a call.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the default stream) and
+ *     return without waiting. Results are ready once the stream reaches that point.
+ *   - Every argument is checked on the host before anything is enqueued; on any
+ *     error nothing is enqueued and the status says why. SPAVA_ERR_HIP reports a
+ *     launch failure; a fault inside a kernel surfaces at the caller's next
+ *     synchronisation.
+ *   - Calls are reentrant. Concurrent calls may share inputs but not outputs or
+ *     workspace.
+ *   - Inputs must be finite. Batch size is 1; one attention layer per call.
+ */
+#ifndef SPAVA_H
+#define SPAVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPAVA_OK = 0,
+  SPAVA_ERR_NULL = 1,       /* a required pointer is NULL                           */
+  SPAVA_ERR_SHAPE = 2,      /* sizes violate the constraints below                  */
+  SPAVA_ERR_DTYPE = 3,      /* unknown dtype                                        */
+  SPAVA_ERR_ALIGN = 4,      /* pointer or stride not 16-byte aligned                */
+  SPAVA_ERR_WORKSPACE = 5,  /* workspace smaller than the size query returned       */
+  SPAVA_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed           */
+  SPAVA_ERR_DEVICE = 7      /* current device is not gfx950                         */
+} spava_status;
+
+typedef enum { SPAVA_BF16 = 0, SPAVA_F32 = 1 } spava_dtype;
+
+/*
+ * Problem shape and tensor layout.
+ *
+ * Layout: q is [N, Hq, d]; k and v are [N, Hkv, d]; out is [N, Hq, d]; element
+ * (t, h, :) of q starts at q + t*q_stride_tok + h*q_stride_head (strides in
+ * ELEMENTS), and the d values are contiguous. k and v share kv_* strides.
+ *
+ * Constraints (else SPAVA_ERR_SHAPE):
+ *   N >= 1, H >= 1, N % H == 0; block length n_b = N / H.      [contiguous blocks]
+ *   Hq >= 1, Hkv >= 1, Hq % Hkv == 0; G = Hq / Hkv; query head hq reads KV head
+ *   hq / G.
+ *   head_dim in {64, 128}.
+ *   0 <= anchor_len A <= n_b          (the anchor, tokens [0, A), lies in block 0)
+ *   passing_len l >= 0                (block j passes l_j = min(l, |C_j|) rows, where
+ *                                      C_0 = [A, n_b) and C_j = block j for j >= 1)
+ *   1 <= window w <= n_b              (observer queries: the last w of each block)
+ *   sm_scale: logit scale; <= 0 selects 1/sqrt(head_dim).
+ *   N * max(Hq, Hkv) * head_dim < 2^31 is not required; offsets are 64-bit.
+ * Alignment (else SPAVA_ERR_ALIGN): tensor pointers 16-byte aligned; strides a
+ * multiple of 8 elements (bf16) or 4 elements (f32).
+ */
+typedef struct {
+  int64_t seq_len;          /* N                                  */
+  int32_t num_hosts;        /* H (virtual hosts = context blocks) */
+  int32_t num_q_heads;      /* Hq                                 */
+  int32_t num_kv_heads;     /* Hkv                                */
+  int32_t head_dim;         /* d                                  */
+  int32_t anchor_len;       /* A                                  */
+  int32_t passing_len;      /* l                                  */
+  int32_t window;           /* w                                  */
+  int32_t dtype;            /* spava_dtype of q, k, v and out     */
+  double sm_scale;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t kv_stride_tok, kv_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+} spava_shape;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* spava_status_string(int status);
+
+/* ABI version of this header: 1. */
+int spava_abi_version(void);
+
+/* Host-only check of a shape (no HIP call). SPAVA_OK or the error it would raise. */
+spava_status spava_validate_shape(const spava_shape* shape);
+
+/* Bytes of workspace spava_select_passing needs for this shape (host only). */
+spava_status spava_select_workspace_bytes(const spava_shape* shape, size_t* bytes);
+
+/* Bytes of workspace spava_approx_attn_fwd needs for this shape (host only). */
+spava_status spava_attn_workspace_bytes(const spava_shape* shape, size_t* bytes);
+
+/*
+ * Passing-block selection ("Passing Blocks": each block forwards its most
+ * essential KV rows, identified by query-to-context attention scores).
+ *
+ * For every block j in [0, H-2] and KV head g, the score of key p of block j is
+ * the mean over the G query heads of group g and the last w queries i of block j
+ * of softmax_p(sm_scale * <q_i, k_p>), the softmax taken over the block's own keys
+ * [s_j, i] (causal, inclusive). Scores are computed in float64. Block j passes the
+ * l_j candidates with the largest scores; equal scores go to the lower position.
+ * The last block's selection is never used and is not computed.
+ *
+ *   q, k         device, dtype per shape, layout above (read only)
+ *   passing_idx  device int32 [max(H-1,0), Hkv, l] (written): for each (j, g) the
+ *                selected positions (absolute token indices) in ascending order,
+ *                then -1 up to l entries
+ *   scores_out   device float64 [H-1, Hkv, n_b] (written) or NULL: the score of every
+ *                key of block j (index p - j*n_b), anchor keys included
+ *   workspace    device, >= spava_select_workspace_bytes bytes (contents scratch)
+ * With H == 1 or l == 0 nothing but the -1 fill (if any) is enqueued.
+ */
+spava_status spava_select_passing(const spava_shape* shape, const void* q, const void* k,
+                                  int32_t* passing_idx, double* scores_out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Approximate attention ("Berechnung": attention over the anchor, the aggregated
+ * passing blocks and the local context).
+ *
+ * For query position i in block h and query head hq (KV head g = hq / G) the
+ * visible keys are: for h >= 1 the anchor [0, A), then the passing rows of blocks
+ * 0..h-1 for head g (in block order); then the local keys [h*n_b, i].
+ *   out[i, hq, :] = sum_p softmax_p(sm_scale * <q_i, k_p>) v_p over that set
+ *   lse_out[hq, i] = log sum_p exp(sm_scale * <q_i, k_p>)   (natural log)
+ * bf16 inputs use bf16 matrix cores with float32 accumulation and softmax, and
+ * round `out` to bf16 (nearest even); f32 inputs compute in float32.
+ *
+ *   q, k, v      device, dtype per shape (read only)
+ *   passing_idx  device int32 [max(H-1,0), Hkv, l] as written by
+ *                spava_select_passing (read only). Block j's entries must lie in
+ *                block j's candidates; an entry outside them is read as a zero row
+ *                (never out of bounds).
+ *   out          device [N, Hq, d] via o_* strides, dtype per shape (written)
+ *   lse_out      device float32 [Hq, N] (written) or NULL
+ *   workspace    device, >= spava_attn_workspace_bytes bytes (contents scratch)
+ */
+spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, const void* k,
+                                   const void* v, const int32_t* passing_idx, void* out,
+                                   float* lse_out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPAVA_H */

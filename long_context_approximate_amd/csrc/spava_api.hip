@@ -1,0 +1,220 @@
+// Host side of the C ABI declared in include/spava.h: argument checks, planning,
+// workspace carving and kernel launches. No device memory is allocated here.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "spava_internal.h"
+
+namespace spava {
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static size_t region(size_t& cursor, size_t bytes) {
+  size_t at = cursor;
+  cursor += static_cast<size_t>(round_up(static_cast<int64_t>(bytes), 256));
+  return at;
+}
+
+static spava_status make_plan(const spava_shape* s, Plan* p) {
+  if (!s) return SPAVA_ERR_NULL;
+  if (s->dtype != SPAVA_BF16 && s->dtype != SPAVA_F32) return SPAVA_ERR_DTYPE;
+  if (s->seq_len < 1 || s->num_hosts < 1 || s->seq_len % s->num_hosts != 0) return SPAVA_ERR_SHAPE;
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1 || s->num_q_heads % s->num_kv_heads != 0)
+    return SPAVA_ERR_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128) return SPAVA_ERR_SHAPE;
+  const int64_t nb = s->seq_len / s->num_hosts;
+  if (nb > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
+  if (s->anchor_len < 0 || s->anchor_len > nb) return SPAVA_ERR_SHAPE;
+  if (s->passing_len < 0) return SPAVA_ERR_SHAPE;
+  if (s->window < 1 || s->window > nb) return SPAVA_ERR_SHAPE;
+  if (!(s->sm_scale == s->sm_scale) || isinf(s->sm_scale)) return SPAVA_ERR_SHAPE;
+  const int64_t unit = s->dtype == SPAVA_BF16 ? 8 : 4;   // elements per 16 bytes
+  const int64_t strides[6] = {s->q_stride_tok, s->q_stride_head, s->kv_stride_tok,
+                              s->kv_stride_head, s->o_stride_tok, s->o_stride_head};
+  for (int64_t st : strides) {
+    if (st < 0) return SPAVA_ERR_SHAPE;
+    if (st % unit != 0) return SPAVA_ERR_ALIGN;
+  }
+  p->N = s->seq_len;
+  p->H = s->num_hosts;
+  p->Hq = s->num_q_heads;
+  p->Hkv = s->num_kv_heads;
+  p->G = s->num_q_heads / s->num_kv_heads;
+  p->D = s->head_dim;
+  p->A = s->anchor_len;
+  p->l = s->passing_len;
+  p->w = s->window;
+  p->nb = static_cast<int>(nb);
+  p->dtype = s->dtype;
+  p->scale = s->sm_scale > 0 ? s->sm_scale : 1.0 / sqrt(static_cast<double>(s->head_dim));
+  p->qs_tok = s->q_stride_tok;
+  p->qs_head = s->q_stride_head;
+  p->kvs_tok = s->kv_stride_tok;
+  p->kvs_head = s->kv_stride_head;
+  p->os_tok = s->o_stride_tok;
+  p->os_head = s->o_stride_head;
+  // Rows each block passes: C_0 excludes the anchor, C_j (j >= 1) is the whole block.
+  const int64_t l0 = p->H > 1 ? std::min<int64_t>(p->l, nb - p->A) : 0;
+  const int64_t l1 = p->H > 2 ? std::min<int64_t>(p->l, nb) : 0;
+  p->l0 = static_cast<int>(l0);
+  p->l1 = static_cast<int>(l1);
+  const int64_t lmax = p->H > 1 ? p->A + l0 + (p->H - 2) * l1 : 0;
+  if (lmax > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
+  p->Lmax = static_cast<int>(lmax);
+  p->Lpad = static_cast<int>(round_up(lmax, kKeyTile));
+  const int64_t R = static_cast<int64_t>(p->G) * p->w;
+  if (R > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
+  p->R = static_cast<int>(R);
+  p->KS = static_cast<int>(cdiv(nb, kScoreSplitKeys));
+  p->T = static_cast<int>(cdiv(nb, kQTile));
+  p->loc_tiles = static_cast<int>(cdiv(nb, kKeyTile));
+  return SPAVA_OK;
+}
+
+SelectWs select_ws_layout(const Plan& p) {
+  SelectWs w{};
+  size_t cur = 0;
+  const size_t jg = static_cast<size_t>(p.H > 1 ? p.H - 1 : 0) * p.Hkv;
+  w.rowstat_part = region(cur, jg * p.KS * p.R * 2 * sizeof(double));
+  w.rowstat = region(cur, jg * p.R * 2 * sizeof(double));
+  w.scores = region(cur, jg * p.nb * sizeof(double));
+  w.total = cur;
+  return w;
+}
+
+AttnWs attn_ws_layout(const Plan& p) {
+  AttnWs w{};
+  size_t cur = 0;
+  const size_t es = p.dtype == SPAVA_BF16 ? 2 : 4;
+  w.kpre = region(cur, static_cast<size_t>(p.Hkv) * p.Lpad * p.D * es);
+  w.vpre = region(cur, static_cast<size_t>(p.Hkv) * p.Lpad * p.D * es);
+  const size_t loc = p.dtype == SPAVA_BF16
+                         ? static_cast<size_t>(p.Hkv) * p.H * p.loc_tiles * kKeyTile * p.D * es
+                         : 0;
+  w.vtloc = region(cur, loc);
+  w.order = region(cur, static_cast<size_t>(p.H) * p.T * sizeof(int32_t));
+  w.total = cur;
+  return w;
+}
+
+// gfx950 check, once per device ordinal.
+static spava_status check_device() {
+  static std::mutex mu;
+  static int known[64];  // 0 unknown, 1 ok, 2 bad
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPAVA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return SPAVA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SPAVA_ERR_HIP;
+    known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return known[dev] == 1 ? SPAVA_OK : SPAVA_ERR_DEVICE;
+}
+
+}  // namespace spava
+
+using namespace spava;
+
+extern "C" {
+
+const char* spava_status_string(int status) {
+  switch (status) {
+    case SPAVA_OK: return "SPAVA_OK";
+    case SPAVA_ERR_NULL: return "SPAVA_ERR_NULL: a required pointer is NULL";
+    case SPAVA_ERR_SHAPE: return "SPAVA_ERR_SHAPE: sizes violate the shape constraints";
+    case SPAVA_ERR_DTYPE: return "SPAVA_ERR_DTYPE: unknown dtype";
+    case SPAVA_ERR_ALIGN: return "SPAVA_ERR_ALIGN: pointer or stride not 16-byte aligned";
+    case SPAVA_ERR_WORKSPACE: return "SPAVA_ERR_WORKSPACE: workspace too small";
+    case SPAVA_ERR_HIP: return "SPAVA_ERR_HIP: HIP runtime call or kernel launch failed";
+    case SPAVA_ERR_DEVICE: return "SPAVA_ERR_DEVICE: current device is not gfx950";
+    default: return "SPAVA: unknown status";
+  }
+}
+
+int spava_abi_version(void) { return 1; }
+
+spava_status spava_validate_shape(const spava_shape* shape) {
+  Plan p;
+  return make_plan(shape, &p);
+}
+
+spava_status spava_select_workspace_bytes(const spava_shape* shape, size_t* bytes) {
+  if (!bytes) return SPAVA_ERR_NULL;
+  Plan p;
+  spava_status st = make_plan(shape, &p);
+  if (st != SPAVA_OK) return st;
+  *bytes = select_ws_layout(p).total;
+  return SPAVA_OK;
+}
+
+spava_status spava_attn_workspace_bytes(const spava_shape* shape, size_t* bytes) {
+  if (!bytes) return SPAVA_ERR_NULL;
+  Plan p;
+  spava_status st = make_plan(shape, &p);
+  if (st != SPAVA_OK) return st;
+  *bytes = attn_ws_layout(p).total;
+  return SPAVA_OK;
+}
+
+spava_status spava_select_passing(const spava_shape* shape, const void* q, const void* k,
+                                  int32_t* passing_idx, double* scores_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Plan p;
+  spava_status st = make_plan(shape, &p);
+  if (st != SPAVA_OK) return st;
+  if (!q || !k) return SPAVA_ERR_NULL;
+  const bool any = p.H > 1 && p.l > 0;
+  if (p.H > 1 && p.l > 0 && !passing_idx) return SPAVA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k)) return SPAVA_ERR_ALIGN;
+  if (passing_idx && (reinterpret_cast<uintptr_t>(passing_idx) & 3u)) return SPAVA_ERR_ALIGN;
+  if (scores_out && (reinterpret_cast<uintptr_t>(scores_out) & 7u)) return SPAVA_ERR_ALIGN;
+  const SelectWs ws = select_ws_layout(p);
+  const bool need_ws = p.H > 1 && (any || scores_out);
+  if (need_ws) {
+    if (!workspace) return SPAVA_ERR_NULL;
+    if (!aligned16(workspace)) return SPAVA_ERR_ALIGN;
+    if (workspace_bytes < ws.total) return SPAVA_ERR_WORKSPACE;
+  }
+  if (p.H == 1) return SPAVA_OK;                 // no block passes anything
+  if (!any && !scores_out) return SPAVA_OK;      // l == 0: the index array is empty
+  st = check_device();
+  if (st != SPAVA_OK) return st;
+  hipError_t e = launch_select(p, q, k, passing_idx, scores_out, static_cast<char*>(workspace),
+                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
+}
+
+spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, const void* k,
+                                   const void* v, const int32_t* passing_idx, void* out,
+                                   float* lse_out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  Plan p;
+  spava_status st = make_plan(shape, &p);
+  if (st != SPAVA_OK) return st;
+  if (!q || !k || !v || !out) return SPAVA_ERR_NULL;
+  if (p.H > 1 && p.l > 0 && !passing_idx) return SPAVA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SPAVA_ERR_ALIGN;
+  if (passing_idx && (reinterpret_cast<uintptr_t>(passing_idx) & 3u)) return SPAVA_ERR_ALIGN;
+  if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)) return SPAVA_ERR_ALIGN;
+  const AttnWs ws = attn_ws_layout(p);
+  if (!workspace) return SPAVA_ERR_NULL;
+  if (!aligned16(workspace)) return SPAVA_ERR_ALIGN;
+  if (workspace_bytes < ws.total) return SPAVA_ERR_WORKSPACE;
+  st = check_device();
+  if (st != SPAVA_OK) return st;
+  hipError_t e;
+  if (p.dtype == SPAVA_BF16)
+    e = launch_attn_bf16(p, q, k, v, passing_idx, out, lse_out, static_cast<char*>(workspace),
+                         static_cast<hipStream_t>(stream));
+  else
+    e = launch_attn_f32(p, q, k, v, passing_idx, out, lse_out, static_cast<char*>(workspace),
+                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
+}
+
+}  // extern "C"

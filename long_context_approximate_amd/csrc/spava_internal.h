@@ -1,0 +1,63 @@
+// Internal definitions shared by the host API and the kernels of libspava.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spava.h"
+
+namespace spava {
+
+constexpr int kKeyTile = 64;     // keys per LDS tile in the attention kernels
+constexpr int kQTile = 256;      // queries per attention workgroup (4 waves x 64)
+constexpr int kScoreTile = 64;   // rows and keys per fp64 score workgroup tile
+constexpr int kScoreSplitKeys = 2048;  // keys per split in the row-statistics pass
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Everything the kernels need about one call, derived on the host from spava_shape.
+struct Plan {
+  int64_t N;
+  int H, Hq, Hkv, G, D, A, l, w;
+  int nb;           // block length N / H
+  int dtype;        // spava_dtype
+  double scale;     // logit scale
+  int64_t qs_tok, qs_head, kvs_tok, kvs_head, os_tok, os_head;
+  int l0, l1;       // rows passed by block 0 and by each block j >= 1
+  int Lmax;         // non-local (anchor + passing) rows of the last block
+  int Lpad;         // Lmax rounded up to a key tile
+  int R;            // observer rows per (block, KV head): G * w
+  int KS;           // key splits of the row-statistics pass
+  int T;            // query tiles per block
+  int loc_tiles;    // key tiles per block
+};
+
+// Non-local prefix length of block h: anchor + passing rows of blocks 0..h-1.
+__host__ __device__ inline int prefix_len(const Plan& p, int h) {
+  return h == 0 ? 0 : p.A + p.l0 + (h - 1) * p.l1;
+}
+
+// Workspace carving (byte offsets, 256-byte aligned regions).
+struct SelectWs {
+  size_t rowstat_part, rowstat, scores, total;
+};
+struct AttnWs {
+  size_t kpre, vpre, vtloc, order, total;
+};
+
+SelectWs select_ws_layout(const Plan& p);
+AttnWs attn_ws_layout(const Plan& p);
+
+// Kernel launchers (defined next to their kernels). They return hipSuccess or the
+// launch error.
+hipError_t launch_select(const Plan& p, const void* q, const void* k, int32_t* idx,
+                         double* scores, char* ws, hipStream_t st);
+hipError_t launch_attn_bf16(const Plan& p, const void* q, const void* k, const void* v,
+                            const int32_t* idx, void* out, float* lse, char* ws,
+                            hipStream_t st);
+hipError_t launch_attn_f32(const Plan& p, const void* q, const void* k, const void* v,
+                           const int32_t* idx, void* out, float* lse, char* ws,
+                           hipStream_t st);
+
+}  // namespace spava

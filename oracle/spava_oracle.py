@@ -43,8 +43,10 @@ Readings where the pages are silent (each is listed in the design notes):
   R8 a query sees its own key (inclusive causal diagonal).
   R9 the last block's selection is never consumed and is not computed.
 
-All arithmetic is float64 on the exact values of the stored inputs. Rows are handled
-in chunks only to bound memory; every row's softmax is computed whole, as defined.
+All arithmetic is float64 on the exact values of the stored inputs. Inputs may be
+passed as stored (bf16 bit patterns as uint16, or float32/float64); every function
+widens exactly the slices it reads. Rows are handled in chunks only to bound memory;
+every row's softmax is computed whole, as defined.
 """
 from __future__ import annotations
 
@@ -150,10 +152,10 @@ def window_scores(sh: Shape, q: np.ndarray, k: np.ndarray, j: int, g: int) -> np
     heads = range(g * G, (g + 1) * G)
     obs_pos = np.arange(e - w, e)                   # observer query positions
     key_pos = np.arange(s, e)                       # local keys of block j
-    kl = k[s:e, g, :]                               # [n_b, d]
+    kl = to_f64(k[s:e, g, :])                       # [n_b, d]
     total = np.zeros(e - s, dtype=np.float64)
     for hq in heads:
-        qw = q[e - w:e, hq, :]                      # [w, d]
+        qw = to_f64(q[e - w:e, hq, :])              # [w, d]
         x = sh.scale * (qw @ kl.T)                  # logits [w, n_b]
         visible = key_pos[None, :] <= obs_pos[:, None]
         x = np.where(visible, x, -np.inf)
@@ -244,14 +246,14 @@ def attention_rows(sh: Shape, q, k, v, idx, hq: int, rows: np.ndarray):
     pre = visible_prefix(sh, idx, h, g)
     local = np.arange(s, e, dtype=np.int64)
     keys = np.concatenate([pre, local])
-    x = sh.scale * (q[rows, hq, :] @ k[keys, g, :].T)           # [R, L_h + n_b]
+    x = sh.scale * (to_f64(q[rows, hq, :]) @ to_f64(k[keys, g, :]).T)   # [R, L_h + n_b]
     hidden = np.zeros(x.shape, dtype=bool)
     hidden[:, len(pre):] = local[None, :] > rows[:, None]       # causal (R8)
     x = np.where(hidden, -np.inf, x)
     m = x.max(axis=1, keepdims=True)
     ex = np.exp(x - m)
     z = ex.sum(axis=1, keepdims=True)
-    o = (ex / z) @ v[keys, g, :]
+    o = (ex / z) @ to_f64(v[keys, g, :])
     lse = m[:, 0] + np.log(z[:, 0])
     return o, lse
 
@@ -282,10 +284,9 @@ def visible_count(sh: Shape, idx: np.ndarray, i: int, g: int) -> int:
 
 def run(sh: Shape, q, k, v, attention: bool = True):
     """Selection then attention on stored inputs; returns a dict of float64 results."""
-    qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
-    scores = all_window_scores(sh, qf, kf)
+    scores = all_window_scores(sh, q, k)
     idx = select_passing(sh, scores)
     out = {"scores": scores, "idx": idx, "margins": selection_margins(sh, scores)}
     if attention:
-        out["o"], out["lse"] = approx_attention(sh, qf, kf, vf, idx)
+        out["o"], out["lse"] = approx_attention(sh, q, k, v, idx)
     return out

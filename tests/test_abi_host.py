@@ -1,0 +1,137 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before anything touches a GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_approximate_amd import spava
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spava.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WS = 0, 1, 2, 3, 4, 5
+FAKE = 0x10000           # aligned non-null address; never dereferenced by these tests
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(spava.LIB_PATH):
+        pytest.skip("libspava.so not built")
+    return spava.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spava_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    declared = _declared_functions()
+    assert declared == sorted(spava.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header(lib):
+    assert ctypes.sizeof(spava.SpavaShape) == 96
+    assert spava.SpavaShape.sm_scale.offset == 40
+    assert lib.spava_abi_version() == 1
+
+
+def _shape(**kw):
+    base = dict(seq_len=4096, num_hosts=4, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                anchor_len=128, passing_len=64, window=32)
+    base.update(kw)
+    return spava.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, OK),
+    ({"seq_len": 4095}, ERR_SHAPE),
+    ({"num_hosts": 0}, ERR_SHAPE),
+    ({"num_q_heads": 7}, ERR_SHAPE),
+    ({"head_dim": 96}, ERR_SHAPE),
+    ({"anchor_len": 1025}, ERR_SHAPE),
+    ({"anchor_len": -1}, ERR_SHAPE),
+    ({"passing_len": -5}, ERR_SHAPE),
+    ({"window": 0}, ERR_SHAPE),
+    ({"window": 1025}, ERR_SHAPE),
+    ({"dtype": 9}, ERR_DTYPE),
+    ({"sm_scale": float("nan")}, ERR_SHAPE),
+    ({"strides": (1028, 128, 256, 128, 1024, 128)}, ERR_ALIGN),
+    ({"num_hosts": 1, "anchor_len": 0}, OK),
+    ({"anchor_len": 1024, "passing_len": 0}, OK),
+])
+def test_shape_validation(lib, kw, status):
+    assert spava.validate_shape(_shape(**kw)) == status
+
+
+def test_null_shape(lib):
+    assert lib.spava_validate_shape(None) == ERR_NULL
+    n = ctypes.c_size_t()
+    assert lib.spava_attn_workspace_bytes(None, ctypes.byref(n)) == ERR_NULL
+    assert lib.spava_attn_workspace_bytes(ctypes.byref(_shape()), None) == ERR_NULL
+
+
+def _expected_ws(sh):
+    def r(b):
+        return (b + 255) // 256 * 256
+    H, hkv, G, w, d = sh.num_hosts, sh.num_kv_heads, sh.num_q_heads // sh.num_kv_heads, \
+        sh.window, sh.head_dim
+    nb = sh.seq_len // H
+    es = 2 if sh.dtype == spava.SPAVA_BF16 else 4
+    ks = -(-nb // 2048)
+    jg = (H - 1) * hkv
+    sel = r(jg * ks * G * w * 16) + r(jg * G * w * 16) + r(jg * nb * 8)
+    l0 = min(sh.passing_len, nb - sh.anchor_len) if H > 1 else 0
+    l1 = min(sh.passing_len, nb) if H > 2 else 0
+    lmax = sh.anchor_len + l0 + (H - 2) * l1 if H > 1 else 0
+    lpad = -(-lmax // 64) * 64
+    attn = 2 * r(hkv * lpad * d * es)
+    attn += r(hkv * H * (-(-nb // 64)) * 64 * d * es) if es == 2 else 0
+    attn += r(H * (-(-nb // 256)) * 4)
+    return sel, attn
+
+
+@pytest.mark.parametrize("kw", [{}, {"num_hosts": 8, "seq_len": 8192}, {"dtype": 1, "head_dim": 64},
+                                {"num_hosts": 2}, {"seq_len": 3000, "num_hosts": 3, "anchor_len": 100}])
+def test_workspace_sizes(lib, kw):
+    sh = _shape(**kw)
+    sel, attn = _expected_ws(sh)
+    assert spava.spava_select_workspace_bytes(sh) == sel
+    assert spava.spava_attn_workspace_bytes(sh) == attn
+
+
+def test_calls_reject_bad_arguments_without_touching_the_gpu(lib):
+    sh = _shape()
+    sel_ws = spava.spava_select_workspace_bytes(sh)
+    attn_ws = spava.spava_attn_workspace_bytes(sh)
+    s = ctypes.byref(sh)
+    f = lib.spava_select_passing
+    assert f(s, None, FAKE, FAKE, None, FAKE, sel_ws, None) == ERR_NULL
+    assert f(s, FAKE, FAKE, None, None, FAKE, sel_ws, None) == ERR_NULL       # idx needed
+    assert f(s, FAKE + 2, FAKE, FAKE, None, FAKE, sel_ws, None) == ERR_ALIGN
+    assert f(s, FAKE, FAKE, FAKE, None, None, sel_ws, None) == ERR_NULL
+    assert f(s, FAKE, FAKE, FAKE, None, FAKE, sel_ws - 1, None) == ERR_WS
+    a = lib.spava_approx_attn_fwd
+    assert a(s, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, attn_ws, None) == ERR_NULL
+    assert a(s, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, attn_ws, None) == ERR_NULL
+    assert a(s, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None, FAKE, attn_ws, None) == ERR_ALIGN
+    assert a(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, attn_ws, None) == ERR_ALIGN
+    assert a(s, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, attn_ws - 1, None) == ERR_WS
+    bad = _shape(seq_len=4095)
+    assert a(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, attn_ws, None) == ERR_SHAPE
+    # One host: nothing to select, returns OK without any device call.
+    one = _shape(num_hosts=1, anchor_len=0)
+    assert f(ctypes.byref(one), FAKE, FAKE, None, None, None, 0, None) == OK
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert spava.status_string(code).startswith("SPAVA")
+    assert "unknown" in spava.status_string(42)
