@@ -1,0 +1,218 @@
+"""Benchmark: Spava / APB-V approximate-attention prefill on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already resident in
+HBM: passing-block selection (fp64 scores + top-l) followed by the approximate
+attention (gather + schedule + bf16 MFMA attention). Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload h8_128k]
+
+`value` is prefill tokens/s (N / step time). `tflops` counts the algorithmic
+attention FLOPs (4 * d * Hq * key-visits over the approximate visible sets, causal
+triangle exact) divided by the attention call's time. `roofline` reports that
+attention call against the bf16 dense MFMA peak; `cpu_baseline` times the fp64
+oracle on a bounded sample on the host cores and extrapolates by work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "approx-attn prefill tokens/s + TFLOP/s (% bf16 MFMA peak), 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_h8_128k_pmc.json")
+ATTN_SOURCE = os.path.join(ROOT, "long_context_approximate_amd", "csrc", "attn_bf16.hip")
+
+
+def key_visits_per_head(cfg) -> int:
+    """Sum over blocks h and their queries i of |V(i)| = L_h + (i - s_h + 1)."""
+    nb, H, A, l = cfg.block_len, cfg.num_hosts, cfg.anchor_len, cfg.passing_len
+    l0 = min(l, nb - A) if H > 1 else 0
+    l1 = min(l, nb)
+    total = 0
+    for h in range(H):
+        L = 0 if h == 0 else A + l0 + (h - 1) * l1
+        total += nb * (nb + 1) // 2 + nb * L
+    return total
+
+
+def attn_flops(cfg) -> float:
+    return 4.0 * cfg.head_dim * cfg.num_q_heads * key_visits_per_head(cfg)
+
+
+def traffic_from_profile():
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary, or None
+    when the summary is missing or the kernel source changed since it was taken."""
+    try:
+        rec = json.load(open(PMC_SUMMARY))
+        src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+        if rec.get("attn_bf16_sha256") != src:
+            return None
+        return float(rec["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(cfg, x, budget_rows=4096, pairs_sampled=2):
+    """Time the fp64 oracle on a sample of the workload and extrapolate to the whole.
+
+    Sample: the window scores + top-l of `pairs_sampled` (block, KV head) pairs, and
+    `budget_rows` query rows of one head in the first, a middle and the last block.
+    The whole-workload time is extrapolated pair-by-pair for selection and by the
+    oracle's own per-row key count (L_h + n_b keys per row) for attention.
+    """
+    import numpy as np
+
+    import oracle
+    sh = oracle.shape_of(cfg)
+    nb, H = cfg.block_len, cfg.num_hosts
+    pairs = max(H - 1, 0) * cfg.num_kv_heads
+    n_pairs = min(pairs_sampled, pairs)
+    t0 = time.perf_counter()
+    for pi in range(n_pairs):
+        j, g = divmod(pi, cfg.num_kv_heads)
+        sc = oracle.window_scores(sh, x["q"], x["k"], j, g)
+        order = np.lexsort((np.arange(nb), -sc))[: cfg.passing_len]
+        del order
+    t_pair = (time.perf_counter() - t0) / max(n_pairs, 1)
+    idx = np.full((max(H - 1, 0), cfg.num_kv_heads, cfg.passing_len), -1, np.int32)
+    for j in range(H - 1):       # a valid selection pattern of the right size
+        cand = oracle.passing_candidates(sh, j)
+        lj = oracle.passing_length(sh, j)
+        idx[j, :, :lj] = cand[:lj]
+    sample_cost = 0.0
+    t_rows = 0.0
+    for h in sorted({0, H // 2, H - 1}):
+        s = h * nb
+        rows = np.arange(s, s + min(budget_rows, nb))
+        L = len(oracle.visible_prefix(sh, idx, h, 0))
+        t1 = time.perf_counter()
+        oracle.attention_rows(sh, x["q"], x["k"], x["v"], idx, 0, rows)
+        t_rows += time.perf_counter() - t1
+        sample_cost += len(rows) * (L + nb)
+    total_cost = 0.0
+    for h in range(H):
+        L = len(oracle.visible_prefix(sh, idx, h, 0))
+        total_cost += nb * (L + nb) * cfg.num_q_heads
+    t_total = t_pair * pairs + t_rows * (total_cost / sample_cost)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return {
+        "value": cfg.seq_len / t_total,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: window scores + top-l of {n_pairs} of {pairs} "
+                   f"(block, kv-head) pairs, and {budget_rows} query rows x 1 head in blocks "
+                   f"{sorted({0, H // 2, H - 1})}; extrapolated by pair count and by the "
+                   f"oracle's per-row key count (measured {t_pair * n_pairs + t_rows:.1f} s, "
+                   f"whole workload est. {t_total:.0f} s)"),
+        "seconds_extrapolated": t_total,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="h8_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the approximate-attention path runs all virtual hosts "
+              "on a single MI355X (no multi-GPU mode). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_approximate_amd import spava
+    from long_context_approximate_amd.inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    x = make_inputs(cfg)
+    dev = spava.device_tensors(x, "cuda:0")
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    shape = spava.shape_from_config(cfg)
+    H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
+    idx = torch.empty((max(H - 1, 0), hkv, l), dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.seq_len, cfg.num_q_heads, cfg.head_dim), dtype=q.dtype, device="cuda")
+    lse = torch.empty((cfg.num_q_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+    ws_sel = torch.empty(max(spava.spava_select_workspace_bytes(shape), 1), dtype=torch.uint8,
+                         device="cuda")
+    ws_attn = torch.empty(max(spava.spava_attn_workspace_bytes(shape), 1), dtype=torch.uint8,
+                          device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        spava.spava_select_passing(shape, q, k, idx, None, ws_sel, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        spava.spava_approx_attn_fwd(shape, q, k, v, idx, out, lse, ws_attn, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_sel = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps / 1e3
+    t_attn = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps / 1e3
+    t_step = wall / args.steps
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    flops = attn_flops(cfg)
+    tflops = flops / t_attn / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": cfg.seq_len / t_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "seq_len": cfg.seq_len, "hosts": H,
+                   "q_heads": cfg.num_q_heads, "kv_heads": hkv, "head_dim": cfg.head_dim,
+                   "anchor": cfg.anchor_len, "passing": l, "window": cfg.window,
+                   "keys": cfg.dist, "parallelism": "single GPU, all hosts in one grid"},
+        "tflops": tflops,
+        "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "attn_tokens_per_s": cfg.seq_len / t_attn,
+        "t_select_ms": t_sel * 1e3,
+        "t_attn_ms": t_attn * 1e3,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_from_profile()},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, x)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
