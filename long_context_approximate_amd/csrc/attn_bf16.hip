@@ -28,10 +28,15 @@
 namespace spava {
 namespace {
 
+#ifndef SPAVA_ATTN_QB
+#define SPAVA_ATTN_QB 1   // 32-query blocks per wave (1: 8 waves of 32 queries, 2 waves/SIMD)
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = kKeyTile;                  // 64 keys per tile
 constexpr int VROWB = BN * 2 + 16;            // bytes per V^T row in LDS (padded)
@@ -42,8 +47,6 @@ struct Cfg {
   static constexpr int KBYTES = BN * KROWB;
   static constexpr int VBYTES = D * VROWB;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KCH = BN * D / 8 / 256; // 16-byte K chunks per thread per tile
-  static constexpr int VCH = D * BN / 8 / 256; // 16-byte V^T chunks per thread per tile
   static constexpr int DK = D / 16;           // MFMA steps over the head dim
   static constexpr int DM = D / 32;           // 32-row blocks of O^T
 };
@@ -164,13 +167,31 @@ __global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restri
   order[rank] = i;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_kernel(
+// Query tile: NW waves x QB 32-query blocks per wave; BM = NW*32*QB = kQTile.
+template <int D, int QB, int NW>
+struct Tile {
+  static constexpr int THREADS = NW * 64;
+  static constexpr int WQ = 32 * QB;             // queries per wave
+  static constexpr int KCH = BN * D / 8 / THREADS; // 16-byte K chunks per thread per tile
+  static constexpr int VCH = D * BN / 8 / THREADS; // 16-byte V^T chunks per thread per tile
+  static_assert(NW * WQ == kQTile, "query tile must match the plan");
+  static_assert(KCH >= 1 && VCH >= 1, "tile too small for the workgroup");
+};
+
+// Softmax rescale threshold (log2 units): the running reference max is only raised
+// when a tile's max exceeds it by more than this, so exp2 values stay <= 2^8 and the
+// accumulators are rescaled rarely. The result is exact: numerator and denominator
+// share the reference.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D, int QB, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(
     Plan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kpre, const uint16_t* __restrict__ vtpre,
     const uint16_t* __restrict__ vtloc, const int32_t* __restrict__ order,
     uint16_t* __restrict__ out, float* __restrict__ lse, int NG, float c_log2) {
   using C = Cfg<D>;
+  using TL = Tile<D, QB, NW>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
 
   // Work item: XCD-aware mapping so the G heads of one KV group run back to back
@@ -196,7 +217,8 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int lr = lane & 31, lh = lane >> 5;
-  const int64_t qw0 = q0 + 64 * w;        // first query of this wave
+  const int64_t qw0 = q0 + static_cast<int64_t>(TL::WQ) * w;   // first query of this wave
+  const int64_t qw_last = qw0 + TL::WQ - 1;
   const bool wave_active = qw0 < e_h;
 
   // ---- tile loaders (global -> registers -> LDS)
@@ -205,76 +227,73 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const uint16_t* vtloc_gh = vtloc + (static_cast<int64_t>(g) * p.H + h) * p.loc_tiles * D * BN;
   const uint16_t* k_g = k + g * p.kvs_head;
 
-  uint4 kreg[C::KCH], vreg[C::VCH];
+  u32x4 kreg[TL::KCH], vreg[TL::VCH];
+  // Branch-free body (only the source pointers depend on the tile kind) so the
+  // staging registers stay in VGPRs.
   auto load_tile = [&](int it) {
-    if (it < npre) {
-      const uint16_t* ks = kpre_g + static_cast<int64_t>(it) * BN * D;
+    const bool pre = it < npre;
+    const int lt = it - npre;
+    const int64_t key0 = s_h + static_cast<int64_t>(lt) * BN;
+    const uint16_t* kb = pre ? kpre_g + static_cast<int64_t>(it) * BN * D : k_g + key0 * p.kvs_tok;
+    const int64_t krow = pre ? D : p.kvs_tok;
+    const int64_t kvalid = pre ? BN : e_h - key0;
+    const uint16_t* vb = pre ? vtpre_g + static_cast<int64_t>(it) * D * BN
+                             : vtloc_gh + static_cast<int64_t>(lt) * D * BN;
 #pragma unroll
-      for (int i = 0; i < C::KCH; ++i) {
-        const int c = tid + 256 * i;
-        kreg[i] = *reinterpret_cast<const uint4*>(ks + c * 8);
-      }
-      const uint16_t* vs = vtpre_g + static_cast<int64_t>(it) * D * BN;
-#pragma unroll
-      for (int i = 0; i < C::VCH; ++i)
-        vreg[i] = *reinterpret_cast<const uint4*>(vs + (tid + 256 * i) * 8);
-    } else {
-      const int lt = it - npre;
-      const int64_t key0 = s_h + static_cast<int64_t>(lt) * BN;
-#pragma unroll
-      for (int i = 0; i < C::KCH; ++i) {
-        const int c = tid + 256 * i;
-        const int row = c / (D / 8), col = c % (D / 8);
-        const int64_t key = key0 + row;
-        kreg[i] = key < e_h ? *reinterpret_cast<const uint4*>(k_g + key * p.kvs_tok + col * 8)
-                            : make_uint4(0, 0, 0, 0);
-      }
-      const uint16_t* vs = vtloc_gh + static_cast<int64_t>(lt) * D * BN;
-#pragma unroll
-      for (int i = 0; i < C::VCH; ++i)
-        vreg[i] = *reinterpret_cast<const uint4*>(vs + (tid + 256 * i) * 8);
+    for (int i = 0; i < TL::KCH; ++i) {
+      const int c = tid + TL::THREADS * i;
+      const int row = c / (D / 8), col = c % (D / 8);
+      kreg[i] = row < kvalid ? *reinterpret_cast<const u32x4*>(kb + row * krow + col * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int i = 0; i < TL::VCH; ++i)
+      vreg[i] = *reinterpret_cast<const u32x4*>(vb + (tid + TL::THREADS * i) * 8);
   };
   auto store_tile = [&](int buf) {
     char* ks = smem + buf * C::STAGE;
     char* vs = ks + C::KBYTES;
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < TL::KCH; ++i) {
+      const int c = tid + TL::THREADS * i;
       const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<uint4*>(ks + row * C::KROWB + col * 16) = kreg[i];
+      *reinterpret_cast<u32x4*>(ks + row * C::KROWB + col * 16) = kreg[i];
     }
 #pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < TL::VCH; ++i) {
+      const int c = tid + TL::THREADS * i;
       const int d = c / (BN / 8), col = c % (BN / 8);
-      *reinterpret_cast<uint4*>(vs + d * VROWB + col * 16) = vreg[i];
+      *reinterpret_cast<u32x4*>(vs + d * VROWB + col * 16) = vreg[i];
     }
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
-  bf16x8 qf[2][C::DK];
+  bf16x8 qf[QB][C::DK];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int64_t qi = qw0 + 32 * qb + lr;
     const bool ok = qi < e_h;
     const uint16_t* qp = q + qi * p.qs_tok + hq * p.qs_head + lh * 8;
 #pragma unroll
     for (int dk = 0; dk < C::DK; ++dk) {
-      uint4 raw = ok ? *reinterpret_cast<const uint4*>(qp + dk * 16) : make_uint4(0, 0, 0, 0);
+      u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(qp + dk * 16) : u32x4{0u, 0u, 0u, 0u};
       qf[qb][dk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
 
-  f32x16 o[2][C::DM];
+  f32x16 o[QB][C::DM];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int dm = 0; dm < C::DM; ++dm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[qb][dm][r] = 0.f;
-  float mrun[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
+  float mrun[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mrun[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+  }
 
   load_tile(0);
   store_tile(0);
@@ -285,13 +304,13 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const bool local = it >= npre;
     const int lt = it - npre;
     const int64_t key0 = local ? s_h + static_cast<int64_t>(lt) * BN : 0;
-    const bool skip = !wave_active || (local && key0 > qw0 + 63);
+    const bool skip = !wave_active || (local && key0 > qw_last);
     if (!skip) {
       const char* ks = smem + (it & 1) * C::STAGE;
       const char* vs = ks + C::KBYTES;
-      f32x16 s[2][2];
+      f32x16 s[QB][2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -303,47 +322,50 @@ __global__ __launch_bounds__(256) void attn_kernel(
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + lr) * C::KROWB +
                                                             (dk * 16 + lh * 8) * 2);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
+          for (int qb = 0; qb < QB; ++qb)
             s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][dk], s[qb][kb], 0, 0, 0);
         }
       }
       // Masks: keys past the prefix length in the last prefix tile; causal on the
       // diagonal local tile.
       const bool pre_tail = !local && it == npre - 1 && (L % BN) != 0;
-      const bool diag = local && key0 + 63 > qw0;
+      const bool diag = local && key0 + BN - 1 > qw0;
       if (pre_tail || diag) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int64_t qi = qw0 + 32 * qb + lr;
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qrel = static_cast<int>(qw0 + 32 * qb + lr - key0);   // query - key0
+          const int lim = pre_tail ? L - it * BN - 1 : qrel;              // last visible kk
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int kk = kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-              const bool hide = pre_tail ? (it * BN + kk >= L) : (key0 + kk > qi);
-              if (hide) s[qb][kb][r] = -INFINITY;
+              if (kk > lim) s[qb][kb][r] = -INFINITY;
             }
         }
       }
-      // Online softmax (log2 domain) and P^T fragments.
-      bf16x8 pf[2][4];
+      // Online softmax (log2 domain, lazy rescale) and P^T fragments.
+      bf16x8 pf[QB][4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun[qb], mx * c_log2);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mref);
-        mrun[qb] = mnew;
-        lsum[qb] *= alpha;
+        const float mt = mx * c_log2;
+        if (__any(mt > mrun[qb] + kRescaleLog2)) {
+          const float mnew = fmaxf(mrun[qb], mt);
+          const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - (mnew == -INFINITY ? 0.f : mnew));
+          mrun[qb] = mnew;
+          lsum[qb] *= alpha;
 #pragma unroll
-        for (int dm = 0; dm < C::DM; ++dm)
+          for (int dm = 0; dm < C::DM; ++dm)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][dm][r] *= alpha;
+            for (int r = 0; r < 16; ++r) o[qb][dm][r] *= alpha;
+        }
+        const float mref = mrun[qb] == -INFINITY ? 0.f : mrun[qb];
         float ps = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (dm * 32 + lr) * VROWB +
                                                             (kc * 16 + lh * 8) * 2);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
+          for (int qb = 0; qb < QB; ++qb)
             o[qb][dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kc], o[qb][dm], 0, 0, 0);
         }
       }
@@ -385,7 +407,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
 
   // ---- epilogue: normalise, round to bf16, write O and LSE
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
     const int64_t qi = qw0 + 32 * qb + lr;
     if (qi >= e_h) continue;
@@ -427,7 +449,9 @@ hipError_t launch_d(const Plan& p, const uint16_t* q, const uint16_t* k, const u
   const int NG = P * p.Hkv;
   const int64_t grid = round_up(NG, 8) * p.G;
   const float c_log2 = static_cast<float>(p.scale * 1.4426950408889634);
-  hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, p, q, k, kpre, vtpre, vtloc, order, out, lse, NG, c_log2);
+  constexpr int QB = SPAVA_ATTN_QB, NW = kQTile / (32 * SPAVA_ATTN_QB);
+  hipLaunchKernelGGL((attn_kernel<D, QB, NW>), dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0,
+                     st, p, q, k, kpre, vtpre, vtloc, order, out, lse, NG, c_log2);
   return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@ import ctypes
 import os
 
 LIB_NAME = "libspava.so"
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+LIB_PATH = os.environ.get("SPAVA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                       LIB_NAME)
 
 SPAVA_BF16 = 0
 SPAVA_F32 = 1
