@@ -9,86 +9,124 @@
 //
 // Kernels, in launch order:
 //   rowstats  (m, z) = (max logit, sum exp(logit - max)) of every observer row over
-//             one key split, register-blocked fp64 dot products staged through LDS;
-//   merge     combine the key splits of each row;
+//             one key split; float64 dot products on v_mfma_f64_16x16x4_f64;
+//   merge     combine the key splits of each row into (m, 1/z);
 //   colsum    per key: sum over all observer rows of exp(x - m) / z, in one fixed
-//             order for every key, then divide by G*w;
+//             order for every key (so equal keys get bitwise-equal scores), then
+//             divide by G*w;
 //   topl      per (j, g): 8-pass MSB radix select on the float64 bit patterns
 //             (scores are >= 0, so unsigned order is numeric order) to find the
 //             l_j-th largest score, then an in-order compaction that keeps every
 //             larger score and the lowest-positioned equal ones.
+//
+// fp64 MFMA 16x16x4 lane layout (wave64): lane l supplies row (l % 16) of A and
+// column (l % 16) of B at reduction slot l / 16; accumulator register r of lane l
+// holds row 4*r + l/16, column l % 16. Each lane therefore owns a contiguous quarter
+// of the head dimension of one row and one key (slot l/16 <-> d in [l/16*D/4, +D/4)).
+// A wave computes a 32-row x 32-key logit tile per step (2 x 2 MFMA blocks).
 #include "spava_internal.h"
 
 namespace spava {
 namespace {
 
-constexpr int kTile = kScoreTile;  // 64 rows x 64 keys per workgroup
-constexpr int kDChunk = 32;        // head-dim slice staged in LDS at a time
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline double to_f64(uint16_t b) {
-  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(b) << 16));
-}
-__device__ inline double to_f64(float f) { return static_cast<double>(f); }
+constexpr int kWaveRows = 32;   // observer rows per wave tile
+constexpr int kWaveKeys = 32;   // keys per wave tile
 
-// Observer row r of (block j, KV head g): head g*G + r / w, query e_j - w + r % w.
-struct RowMap {
-  __device__ static int64_t token(const Plan& p, int j, int r) {
-    return static_cast<int64_t>(j + 1) * p.nb - p.w + (r % p.w);
+// One lane's quarter-row of q or k (D/4 consecutive elements), kept as stored bits.
+template <typename T, int D>
+struct Frag;
+
+template <int D>
+struct Frag<uint16_t, D> {
+  static constexpr int W = D / 8;  // 32-bit words (2 bf16 each)
+  uint32_t w[W];
+  __device__ void load(const uint16_t* ptr, bool ok) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(ptr + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+      w[4 * i] = v[0];
+      w[4 * i + 1] = v[1];
+      w[4 * i + 2] = v[2];
+      w[4 * i + 3] = v[3];
+    }
   }
-  __device__ static int head(const Plan& p, int g, int r) { return g * p.G + r / p.w; }
+  __device__ double at(int s) const {
+    const uint32_t x = w[s >> 1];
+    const uint32_t b = (s & 1) ? (x & 0xFFFF0000u) : (x << 16);
+    return static_cast<double>(__uint_as_float(b));
+  }
 };
 
-// 64x64 tile of logits (unscaled dot products) for rows [r0, r0+64) and keys
-// [c0, c0+64) of block j; each thread owns rows tr+16a and keys tk+16b.
-template <typename T>
-__device__ inline void tile_dots(const Plan& p, const T* q, const T* k, int j, int g, int r0,
-                                 int64_t key0, double (*Qs)[kTile + 1], double (*Ks)[kTile + 1],
-                                 int64_t* q_off, int64_t* k_tok, double acc[4][4]) {
-  const int tid = threadIdx.x, tr = tid >> 4, tk = tid & 15;
-  const int64_t e = static_cast<int64_t>(j + 1) * p.nb;
-  if (tid < kTile) {
-    const int r = r0 + tid;
-    q_off[tid] = r < p.R ? RowMap::token(p, j, r) * p.qs_tok + RowMap::head(p, g, r) * p.qs_head
-                         : -1;
-    const int64_t key = key0 + tid;
-    k_tok[tid] = key < e ? key : -1;
+template <int D>
+struct Frag<float, D> {
+  static constexpr int W = D / 4;
+  uint32_t w[W];
+  __device__ void load(const float* ptr, bool ok) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(ptr + 4 * i) : u32x4{0u, 0u, 0u, 0u};
+      w[4 * i] = v[0];
+      w[4 * i + 1] = v[1];
+      w[4 * i + 2] = v[2];
+      w[4 * i + 3] = v[3];
+    }
   }
+  __device__ double at(int s) const { return static_cast<double>(__uint_as_float(w[s])); }
+};
+
+// Observer row r of (block j, KV head g): head g*G + r / w, query e_j - w + r % w.
+__device__ inline int64_t row_token(const Plan& p, int j, int r) {
+  return static_cast<int64_t>(j + 1) * p.nb - p.w + (r % p.w);
+}
+__device__ inline int row_head(const Plan& p, int g, int r) { return g * p.G + r / p.w; }
+
+// 32x32 tile of unscaled logits: acc[rb][kb] holds rows rb*16 + 4*r + l/16 and key
+// kb*16 + l%16 of the tile.
+template <typename T, int D>
+__device__ inline void tile_logits(const Frag<T, D> (&qa)[2], const Frag<T, D> (&kf)[2],
+                                   f64x4 (&acc)[2][2]) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int dc = 0; dc < p.D / kDChunk; ++dc) {
-    __syncthreads();
-    {
-      // Q rows: gather by precomputed element offsets.
-      const int r = tid >> 2, part = tid & 3;
-      const int64_t off = q_off[r];
+    for (int kb = 0; kb < 2; ++kb) acc[rb][kb] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int dd = part * 8 + t;
-        Qs[dd][r] = off >= 0 ? to_f64(q[off + dc * kDChunk + dd]) : 0.0;
-      }
-      const int64_t tok = k_tok[r];
-      const T* kb = k + g * p.kvs_head;
+  for (int s = 0; s < D / 4; ++s) {
+    const double a0 = qa[0].at(s), a1 = qa[1].at(s);
+    const double b0 = kf[0].at(s), b1 = kf[1].at(s);
+    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+
+// Load the lane's A fragments (observer rows r0 + rb*16 + l%16) for (j, g).
+template <typename T, int D>
+__device__ inline void load_rows(const Plan& p, const T* q, int j, int g, int r0, int col, int kg,
+                                 Frag<T, D> (&qa)[2]) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int dd = part * 8 + t;
-        Ks[dd][r] = tok >= 0 ? to_f64(kb[tok * p.kvs_tok + dc * kDChunk + dd]) : 0.0;
-      }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int dd = 0; dd < kDChunk; ++dd) {
-      double qa[4], kv[4];
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = r0 + rb * 16 + col;
+    const bool ok = r < p.R;
+    const int rr = ok ? r : 0;
+    const T* ptr = q + row_token(p, j, rr) * p.qs_tok + row_head(p, g, rr) * p.qs_head + kg * (D / 4);
+    qa[rb].load(ptr, ok);
+  }
+}
+
+// Load the lane's B fragments (keys key0 + kb*16 + l%16, valid below key_end).
+template <typename T, int D>
+__device__ inline void load_keys(const Plan& p, const T* k, int g, int64_t key0, int64_t key_end,
+                                 int col, int kg, Frag<T, D> (&kf)[2]) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) qa[a] = Qs[dd][tr + 16 * a];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) kv[b] = Ks[dd][tk + 16 * b];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(qa[a], kv[b], acc[a][b]);
-    }
+  for (int kb = 0; kb < 2; ++kb) {
+    const int64_t key = key0 + kb * 16 + col;
+    const bool ok = key < key_end;
+    const T* ptr = k + (ok ? key : 0) * p.kvs_tok + g * p.kvs_head + kg * (D / 4);
+    kf[kb].load(ptr, ok);
   }
 }
 
@@ -102,68 +140,86 @@ __device__ inline void lse_merge(double& m, double& z, double mo, double zo) {
   m = mn;
 }
 
-template <typename T>
+// One wave per (jg, 32-row tile, key split). Waves are independent (no barriers).
+template <typename T, int D>
 __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restrict__ q,
                                                        const T* __restrict__ k,
-                                                       double2* __restrict__ part) {
-  __shared__ double Qs[kDChunk][kTile + 1];
-  __shared__ double Ks[kDChunk][kTile + 1];
-  __shared__ int64_t q_off[kTile], k_tok[kTile];
-  const int r0 = blockIdx.x * kTile;
-  const int split = blockIdx.y;
-  const int jg = blockIdx.z;
+                                                       double2* __restrict__ part,
+                                                       int row_tiles) {
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t total = static_cast<int64_t>(p.H - 1) * p.Hkv * row_tiles * p.KS;
+  if (wid >= total) return;
+  const int split = static_cast<int>(wid % p.KS);
+  const int64_t rest = wid / p.KS;
+  const int rt = static_cast<int>(rest % row_tiles);
+  const int jg = static_cast<int>(rest / row_tiles);
   const int j = jg / p.Hkv, g = jg % p.Hkv;
-  const int tid = threadIdx.x, tr = tid >> 4, tk = tid & 15;
+  const int lane = threadIdx.x & 63, col = lane & 15, kg = lane >> 4;
   const int64_t s = static_cast<int64_t>(j) * p.nb;
   const int64_t split_lo = s + static_cast<int64_t>(split) * kScoreSplitKeys;
   const int64_t split_hi = min(s + p.nb, split_lo + kScoreSplitKeys);
+  const int r0 = rt * kWaveRows;
 
-  double m[4], z[4];
-  int64_t qi[4];
+  Frag<T, D> qa[2];
+  load_rows<T, D>(p, q, j, g, r0, col, kg, qa);
+  double m[2][4], z[2][4];
+  int64_t qi[2][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    m[a] = -INFINITY;
-    z[a] = 0.0;
-    const int r = r0 + tr + 16 * a;
-    qi[a] = r < p.R ? RowMap::token(p, j, r) : -1;   // -1: padding row sees nothing
-  }
-  for (int64_t key0 = split_lo; key0 < split_hi; key0 += kTile) {
-    double acc[4][4];
-    tile_dots(p, q, k, j, g, r0, key0, Qs, Ks, q_off, k_tok, acc);
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      double x[4];
-      bool vis[4];
-      double mt = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t key = key0 + tk + 16 * b;
-        vis[b] = key < split_hi && key <= qi[a];
-        x[b] = p.scale * acc[a][b];
-        if (vis[b]) mt = fmax(mt, x[b]);
-      }
-      if (mt > m[a]) {
-        z[a] = (m[a] == -INFINITY) ? 0.0 : z[a] * exp(m[a] - mt);
-        m[a] = mt;
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (vis[b]) z[a] += exp(x[b] - m[a]);
+    for (int rr = 0; rr < 4; ++rr) {
+      m[rb][rr] = -INFINITY;
+      z[rb][rr] = 0.0;
+      const int r = r0 + rb * 16 + 4 * rr + kg;
+      qi[rb][rr] = r < p.R ? row_token(p, j, r) : -1;   // -1: padding row sees nothing
     }
+  Frag<T, D> kf[2];
+  load_keys<T, D>(p, k, g, split_lo, split_hi, col, kg, kf);
+  for (int64_t key0 = split_lo; key0 < split_hi; key0 += kWaveKeys) {
+    f64x4 acc[2][2];
+    tile_logits<T, D>(qa, kf, acc);
+    // Prefetch the next key tile while this tile's softmax statistics are formed.
+    if (key0 + kWaveKeys < split_hi)
+      load_keys<T, D>(p, k, g, key0 + kWaveKeys, split_hi, col, kg, kf);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        double x[2];
+        bool vis[2];
+        double mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int64_t key = key0 + kb * 16 + col;
+          vis[kb] = key < split_hi && key <= qi[rb][rr];
+          x[kb] = p.scale * acc[rb][kb][rr];
+          if (vis[kb]) mt = fmax(mt, x[kb]);
+        }
+        if (mt > m[rb][rr]) {
+          z[rb][rr] = (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp(m[rb][rr] - mt);
+          m[rb][rr] = mt;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          if (vis[kb]) z[rb][rr] += exp(x[kb] - m[rb][rr]);
+      }
   }
-  // Reduce over the 16 lanes (tk) that share each row.
+  // Reduce over the 16 lanes (l % 16) that hold different keys of the same rows.
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      const double mo = __shfl_xor(m[a], off);
-      const double zo = __shfl_xor(z[a], off);
-      lse_merge(m[a], z[a], mo, zo);
+    for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        const double mo = __shfl_xor(m[rb][rr], off);
+        const double zo = __shfl_xor(z[rb][rr], off);
+        lse_merge(m[rb][rr], z[rb][rr], mo, zo);
+      }
+      const int r = r0 + rb * 16 + 4 * rr + kg;
+      if (col == 0 && r < p.R)
+        part[(static_cast<int64_t>(jg) * p.KS + split) * p.R + r] =
+            make_double2(m[rb][rr], z[rb][rr]);
     }
-    const int r = r0 + tr + 16 * a;
-    if (tk == 0 && r < p.R)
-      part[(static_cast<int64_t>(jg) * p.KS + split) * p.R + r] = make_double2(m[a], z[a]);
-  }
 }
 
 __global__ void merge_kernel(Plan p, const double2* __restrict__ part,
@@ -178,55 +234,68 @@ __global__ void merge_kernel(Plan p, const double2* __restrict__ part,
     const double2 pr = part[(jg * p.KS + sidx) * p.R + r];
     lse_merge(m, z, pr.x, pr.y);
   }
-  rowstat[t] = make_double2(m, z);
+  rowstat[t] = make_double2(m, 1.0 / z);   // (max, 1 / sum)
 }
 
-template <typename T>
+// One wave per (jg, 32-key tile); loops over all observer rows in a fixed order.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void colsum_kernel(Plan p, const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const double2* __restrict__ rowstat,
-                                                     double* __restrict__ scores) {
-  __shared__ double Qs[kDChunk][kTile + 1];
-  __shared__ double Ks[kDChunk][kTile + 1];
-  __shared__ int64_t q_off[kTile], k_tok[kTile];
-  __shared__ double red[16][kTile + 1];
-  const int kt = blockIdx.x;
-  const int jg = blockIdx.y;
+                                                     double* __restrict__ scores, int key_tiles) {
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t total = static_cast<int64_t>(p.H - 1) * p.Hkv * key_tiles;
+  if (wid >= total) return;
+  const int kt = static_cast<int>(wid % key_tiles);
+  const int jg = static_cast<int>(wid / key_tiles);
   const int j = jg / p.Hkv, g = jg % p.Hkv;
-  const int tid = threadIdx.x, tr = tid >> 4, tk = tid & 15;
+  const int lane = threadIdx.x & 63, col = lane & 15, kg = lane >> 4;
   const int64_t s = static_cast<int64_t>(j) * p.nb;
-  const int64_t key0 = s + static_cast<int64_t>(kt) * kTile;
+  const int64_t e = s + p.nb;
+  const int64_t key0 = s + static_cast<int64_t>(kt) * kWaveKeys;
 
-  double col[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int r0 = 0; r0 < p.R; r0 += kTile) {
-    double acc[4][4];
-    tile_dots(p, q, k, j, g, r0, key0, Qs, Ks, q_off, k_tok, acc);
+  Frag<T, D> kf[2];
+  load_keys<T, D>(p, k, g, key0, e, col, kg, kf);
+  int64_t key[2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int r = r0 + tr + 16 * a;
-      const bool row_ok = r < p.R;
-      const int64_t qi = row_ok ? RowMap::token(p, j, r) : -1;
-      const double2 st = row_ok ? rowstat[static_cast<int64_t>(jg) * p.R + r] : make_double2(0, 1);
+  for (int kb = 0; kb < 2; ++kb) key[kb] = key0 + kb * 16 + col;
+  const double2* st = rowstat + static_cast<int64_t>(jg) * p.R;
+
+  double colsum[2] = {0.0, 0.0};
+  Frag<T, D> qa[2];
+  load_rows<T, D>(p, q, j, g, 0, col, kg, qa);
+  for (int r0 = 0; r0 < p.R; r0 += kWaveRows) {
+    f64x4 acc[2][2];
+    tile_logits<T, D>(qa, kf, acc);
+    // Prefetch the next observer rows while this tile's probabilities are summed.
+    if (r0 + kWaveRows < p.R) load_rows<T, D>(p, q, j, g, r0 + kWaveRows, col, kg, qa);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t key = key0 + tk + 16 * b;
-        const double x = p.scale * acc[a][b];
-        const double pi = (row_ok && key <= qi) ? exp(x - st.x) / st.y : 0.0;
-        col[b] += pi;
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = r0 + rb * 16 + 4 * rr + kg;
+        const bool ok = r < p.R;
+        const double2 mz = ok ? st[r] : make_double2(0.0, 0.0);
+        const int64_t qi = ok ? row_token(p, j, r) : -1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const double x = p.scale * acc[rb][kb][rr];
+          colsum[kb] += key[kb] <= qi ? exp(x - mz.x) * mz.y : 0.0;
+        }
       }
-    }
   }
+  // The four lanes col, col+16, col+32, col+48 hold disjoint row sets of the same key;
+  // add them in a fixed order.
 #pragma unroll
-  for (int b = 0; b < 4; ++b) red[tr][tk + 16 * b] = col[b];
-  __syncthreads();
-  if (tid < kTile) {
-    const int64_t key = key0 + tid;
-    if (key < s + p.nb) {
-      double sum = 0.0;
-      for (int t = 0; t < 16; ++t) sum += red[t][tid];
-      scores[static_cast<int64_t>(jg) * p.nb + (key - s)] =
+  for (int kb = 0; kb < 2; ++kb) {
+    const double v0 = __shfl(colsum[kb], col);
+    const double v1 = __shfl(colsum[kb], col + 16);
+    const double v2 = __shfl(colsum[kb], col + 32);
+    const double v3 = __shfl(colsum[kb], col + 48);
+    const double sum = ((v0 + v1) + v2) + v3;
+    if (kg == 0 && key[kb] < e)
+      scores[static_cast<int64_t>(jg) * p.nb + (key[kb] - s)] =
           sum / static_cast<double>(static_cast<int64_t>(p.G) * p.w);
-    }
   }
 }
 
@@ -330,32 +399,43 @@ __global__ __launch_bounds__(1024) void topl_kernel(Plan p, const double* __rest
 
 }  // namespace
 
-template <typename T>
+template <typename T, int D>
 static hipError_t launch_select_t(const Plan& p, const T* q, const T* k, int32_t* idx,
                                   double* scores_out, char* ws, hipStream_t st) {
   const SelectWs w = select_ws_layout(p);
   double2* part = reinterpret_cast<double2*>(ws + w.rowstat_part);
   double2* rowstat = reinterpret_cast<double2*>(ws + w.rowstat);
   double* scores = scores_out ? scores_out : reinterpret_cast<double*>(ws + w.scores);
-  const int JG = (p.H - 1) * p.Hkv;
-  dim3 g1(static_cast<unsigned>(cdiv(p.R, kTile)), p.KS, JG);
-  hipLaunchKernelGGL(rowstats_kernel<T>, g1, dim3(256), 0, st, p, q, k, part);
-  const int64_t rows = static_cast<int64_t>(JG) * p.R;
+  const int64_t JG = static_cast<int64_t>(p.H - 1) * p.Hkv;
+  const int row_tiles = static_cast<int>(cdiv(p.R, kWaveRows));
+  const int64_t w1 = JG * row_tiles * p.KS;
+  hipLaunchKernelGGL((rowstats_kernel<T, D>), dim3(static_cast<unsigned>(cdiv(w1, 4))), dim3(256),
+                     0, st, p, q, k, part, row_tiles);
+  const int64_t rows = JG * p.R;
   hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(cdiv(rows, 256))), dim3(256), 0, st,
                      p, part, rowstat);
-  dim3 g3(static_cast<unsigned>(cdiv(p.nb, kTile)), JG);
-  hipLaunchKernelGGL(colsum_kernel<T>, g3, dim3(256), 0, st, p, q, k, rowstat, scores);
-  if (p.l > 0) hipLaunchKernelGGL(topl_kernel, dim3(JG), dim3(1024), 0, st, p, scores, idx);
+  const int key_tiles = static_cast<int>(cdiv(p.nb, kWaveKeys));
+  const int64_t w3 = JG * key_tiles;
+  hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(static_cast<unsigned>(cdiv(w3, 4))), dim3(256), 0,
+                     st, p, q, k, rowstat, scores, key_tiles);
+  if (p.l > 0)
+    hipLaunchKernelGGL(topl_kernel, dim3(static_cast<unsigned>(JG)), dim3(1024), 0, st, p, scores,
+                       idx);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const Plan& p, const void* q, const void* k, int32_t* idx,
                          double* scores, char* ws, hipStream_t st) {
-  if (p.dtype == SPAVA_BF16)
-    return launch_select_t(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                           idx, scores, ws, st);
-  return launch_select_t(p, static_cast<const float*>(q), static_cast<const float*>(k), idx,
-                         scores, ws, st);
+  if (p.dtype == SPAVA_BF16) {
+    auto qq = static_cast<const uint16_t*>(q);
+    auto kk = static_cast<const uint16_t*>(k);
+    if (p.D == 128) return launch_select_t<uint16_t, 128>(p, qq, kk, idx, scores, ws, st);
+    return launch_select_t<uint16_t, 64>(p, qq, kk, idx, scores, ws, st);
+  }
+  auto qq = static_cast<const float*>(q);
+  auto kk = static_cast<const float*>(k);
+  if (p.D == 128) return launch_select_t<float, 128>(p, qq, kk, idx, scores, ws, st);
+  return launch_select_t<float, 64>(p, qq, kk, idx, scores, ws, st);
 }
 
 }  // namespace spava
