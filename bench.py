@@ -60,7 +60,7 @@ def traffic_from_profile():
         return None
 
 
-def cpu_baseline(cfg, x, budget_rows=4096, pairs_sampled=2):
+def cpu_baseline(cfg, x, budget_rows=16384, pairs_sampled=8):
     """Time the fp64 oracle on a sample of the workload and extrapolate to the whole.
 
     Sample: the window scores + top-l of `pairs_sampled` (block, KV head) pairs, and

@@ -77,6 +77,15 @@ struct Frag<float, D> {
   __device__ double at(int s) const { return static_cast<double>(__uint_as_float(w[s])); }
 };
 
+// Keep a loop-invariant fragment as stored bits: the empty asm tells the compiler the
+// words may change, so the fp64 widening is redone per use instead of hoisted into
+// 2x as many registers (which would cap occupancy at one wave per SIMD).
+template <typename F>
+__device__ inline void opaque(F& f) {
+#pragma unroll
+  for (int i = 0; i < F::W; ++i) asm volatile("" : "+v"(f.w[i]));
+}
+
 // Observer row r of (block j, KV head g): head g*G + r / w, query e_j - w + r % w.
 __device__ inline int64_t row_token(const Plan& p, int j, int r) {
   return static_cast<int64_t>(j + 1) * p.nb - p.w + (r % p.w);
@@ -176,6 +185,8 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
   Frag<T, D> kf[2];
   load_keys<T, D>(p, k, g, split_lo, split_hi, col, kg, kf);
   for (int64_t key0 = split_lo; key0 < split_hi; key0 += kWaveKeys) {
+    opaque(qa[0]);
+    opaque(qa[1]);
     f64x4 acc[2][2];
     tile_logits<T, D>(qa, kf, acc);
     // Prefetch the next key tile while this tile's softmax statistics are formed.
@@ -265,6 +276,8 @@ __global__ __launch_bounds__(256) void colsum_kernel(Plan p, const T* __restrict
   Frag<T, D> qa[2];
   load_rows<T, D>(p, q, j, g, 0, col, kg, qa);
   for (int r0 = 0; r0 < p.R; r0 += kWaveRows) {
+    opaque(kf[0]);
+    opaque(kf[1]);
     f64x4 acc[2][2];
     tile_logits<T, D>(qa, kf, acc);
     // Prefetch the next observer rows while this tile's probabilities are summed.
