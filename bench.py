@@ -122,6 +122,54 @@ def cpu_baseline(cfg, x, budget_rows=16384, pairs_sampled=8):
     }
 
 
+def _time_call(fn, stream, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_schedules(shape, q, k, v, idx, out, lse, ws, stream, reps=3):
+    """Attention-call time under each dispatch order (same results, different timing)."""
+    from long_context_approximate_amd import spava
+    res = {}
+    prev = os.environ.get("SPAVA_SCHEDULE")
+    for mode in ("lpt", "zigzag", "natural"):
+        os.environ["SPAVA_SCHEDULE"] = mode
+        res[mode] = _time_call(
+            lambda: spava.spava_approx_attn_fwd(shape, q, k, v, idx, out, lse, ws, stream),
+            stream, reps)
+    if prev is None:
+        os.environ.pop("SPAVA_SCHEDULE", None)
+    else:
+        os.environ["SPAVA_SCHEDULE"] = prev
+    return res
+
+
+def dense_baseline(cfg, q, k, v, stream, t_step, reps=3):
+    """Dense causal attention (one host: nothing passed, every key local) on the same
+    inputs and the same kernel: the one-GPU analogue of the FlashAttention baseline."""
+    import torch
+
+    from long_context_approximate_amd import spava
+    dense = cfg.with_(num_hosts=1, anchor_len=0, passing_len=0, window=1)
+    shape = spava.shape_from_config(dense)
+    out = torch.empty_like(q)
+    ws = torch.empty(spava.spava_attn_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((0, cfg.num_kv_heads, 0), dtype=torch.int32, device="cuda")
+    ms = _time_call(lambda: spava.spava_approx_attn_fwd(shape, q, k, v, idx, out, None, ws, stream),
+                    stream, reps)
+    flops = attn_flops(dense)
+    return {"attn_ms": ms, "tflops": flops / ms / 1e9, "flops": flops,
+            "approx_step_speedup": ms / (t_step * 1e3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +177,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="h8_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dense (one host) baseline and the schedule comparison")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -218,6 +268,9 @@ def main():
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_from_profile()},
     }
+    if not args.no_extras:
+        rec["schedules_attn_ms"] = time_schedules(shape, q, k, v, idx, out, lse, ws_attn, stream)
+        rec["dense_causal"] = dense_baseline(cfg, q, k, v, stream, t_step)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, x)
     print(json.dumps(rec), flush=True)

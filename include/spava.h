@@ -11,10 +11,18 @@
  * blocks: the l most important key/value rows each earlier block forwards, chosen
  * by query-to-context attention scores. Here all H "hosts" run on one GPU.
  *
- * Two calls make one prefill layer:
+ * Two calls make one prefill layer over the context:
  *   spava_select_passing   scores every key of blocks 0..H-2 and picks each
  *                          block's passing rows per KV head;
  *   spava_approx_attn_fwd  gathers anchor + passing rows and runs the attention.
+ * A third call attends a query block (the text question after the context) to the
+ * whole context exactly, by per-host partials merged with their log-sum-exp:
+ *   spava_query_attn_fwd.
+ *
+ * The environment variable SPAVA_SCHEDULE (lpt | natural | zigzag) selects the
+ * dispatch order of the attention's query tiles: longest first (default), block
+ * order, or the pages' ZigZag host pairing (h, H-1-h). It changes timing only,
+ * never results.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
@@ -154,6 +162,37 @@ spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, cons
                                    const void* v, const int32_t* passing_idx, void* out,
                                    float* lse_out, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/* Bytes of workspace spava_query_attn_fwd needs for n_query query rows (host only). */
+spava_status spava_query_workspace_bytes(const spava_shape* shape, int64_t n_query,
+                                         size_t* bytes);
+
+/*
+ * Query block B_qr (explainer "APB-V: ...", Methodik > Kontext-Splitting: the input is
+ * split into anchor, query block and context blocks; Systemseitige Optimierungen >
+ * fused context + query forward: each host attends the query rows to what it holds
+ * and the partial results are merged with their log-sum-exp).
+ *
+ * The n_query rows of B_qr follow the N context tokens. Row i attends to every
+ * context key [0, N) and to the query keys [0, i]:
+ *   out_qr[i, hq, :] = sum_p softmax_p(sm_scale * <q_qr_i, k_p>) v_p over that set
+ *   lse_qr[hq, i]    = log sum_p exp(sm_scale * <q_qr_i, k_p>)      (natural log)
+ * computed as H + 1 partials over disjoint key sets (each context block, then the
+ * query block itself) merged by log-sum-exp, which is exact.
+ *
+ *   shape        the context's shape; its q/kv/o strides also describe q_qr, k_qr,
+ *                v_qr and out_qr. anchor_len, passing_len and window are not used.
+ *   n_query      1 <= n_query <= 2^30
+ *   q_qr         device [n_query, Hq, d]; k_qr, v_qr device [n_query, Hkv, d]
+ *   k, v         device context [N, Hkv, d]
+ *   out_qr       device [n_query, Hq, d], dtype per shape (written)
+ *   lse_qr       device float32 [Hq, n_query] (written) or NULL
+ *   workspace    device, >= spava_query_workspace_bytes bytes (contents scratch)
+ */
+spava_status spava_query_attn_fwd(const spava_shape* shape, int64_t n_query, const void* q_qr,
+                                  const void* k_qr, const void* v_qr, const void* k,
+                                  const void* v, void* out_qr, float* lse_qr, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["spava_api.hip", "select.hip", "attn_bf16.hip", "attn_f32.hip"]
+SOURCES = ["spava_api.hip", "select.hip", "attn_bf16.hip", "attn_f32.hip", "attn_query.hip"]
 OUT = os.path.join(HERE, "libspava.so")
 
 HIPCC_FLAGS = [

@@ -1,0 +1,236 @@
+// Device pieces shared by the bf16 attention kernels (approximate attention over
+// [anchor | passing | local causal] and the query-block partials): LDS tile layout,
+// the V^T key-slot order, and one flash-attention step over a 64-key tile.
+//
+// MFMA 32x32x16 bf16 operand layout (wave64): lane l supplies row/column (l % 32) of
+// A/B and 8 consecutive reduction slots selected by (l / 32); accumulator register r
+// of lane l holds row 8*(r/4) + 4*(l/32) + (r%4), column l % 32. Computing S^T (keys x
+// queries) leaves each lane with one query and 16 keys per 32-key block, which is
+// exactly the B operand P^T of the second product once V^T's key slots are stored in
+// the same order; so P never leaves registers.
+#pragma once
+
+#include "spava_internal.h"
+
+namespace spava {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BN = kKeyTile;                  // 64 keys per tile
+constexpr int VROWB = BN * 2 + 16;            // bytes per V^T row in LDS (padded)
+constexpr int kWaves = 8;                     // waves per attention workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kWaveQ = 32;                    // queries per wave
+static_assert(kWaves * kWaveQ == kQTile, "query tile must match the plan");
+
+// Softmax rescale threshold (log2 units): the running reference max is only raised
+// when a tile's max exceeds it by more than this, so exp2 values stay <= 2^8 and the
+// accumulators are rescaled rarely. The result is exact: numerator and denominator
+// share the reference.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D>
+struct Cfg {
+  static constexpr int KROWB = D * 2 + 16;    // bytes per K row in LDS (padded)
+  static constexpr int KBYTES = BN * KROWB;
+  static constexpr int VBYTES = D * VROWB;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int DK = D / 16;           // MFMA steps over the head dim
+  static constexpr int DM = D / 32;           // 32-row blocks of O^T
+  static constexpr int KCH = BN * D / 8 / kThreads;   // 16-byte K chunks per thread per tile
+  static constexpr int VCH = D * BN / 8 / kThreads;   // 16-byte V^T chunks per thread per tile
+  static_assert(KCH >= 1 && VCH >= 1, "tile too small for the workgroup");
+};
+
+// Key offset inside a 16-key chunk for MFMA reduction slot s (an involution).
+__host__ __device__ constexpr int slot_key(int s) {
+  return 8 * ((s & 7) >> 2) + 4 * (s >> 3) + (s & 3);
+}
+
+// Write one 64-key V^T tile [D][64] (slot order) to global memory from 64 V rows
+// staged in LDS as Vs[row][D + 8]; called by all 256 threads of a workgroup.
+template <int D>
+__device__ inline void store_vt_tile(const uint16_t (*Vs)[D + 8], uint16_t* dst) {
+  for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
+    const int d = c / (BN / 8), sc = c % (BN / 8);   // slots sc*8 .. sc*8+7
+    uint16_t vals[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int slot = sc * 8 + e;
+      const int key = (slot & ~15) + slot_key(slot & 15);
+      vals[e] = Vs[key][d];
+    }
+    uint4 pk;
+    pk.x = vals[0] | (static_cast<uint32_t>(vals[1]) << 16);
+    pk.y = vals[2] | (static_cast<uint32_t>(vals[3]) << 16);
+    pk.z = vals[4] | (static_cast<uint32_t>(vals[5]) << 16);
+    pk.w = vals[6] | (static_cast<uint32_t>(vals[7]) << 16);
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(d) * BN + sc * 8) = pk;
+  }
+}
+
+// Global -> register staging of one tile (K rows and a V^T tile) and the register ->
+// LDS store, for a workgroup of kThreads threads. `kb`/`krow`/`kvalid` describe the K
+// rows (element pointer, row stride, rows present); rows past kvalid are zero.
+template <int D>
+struct TileStage {
+  u32x4 kreg[Cfg<D>::KCH], vreg[Cfg<D>::VCH];
+  __device__ void load(const uint16_t* kb, int64_t krow, int64_t kvalid, const uint16_t* vb) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < Cfg<D>::KCH; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / (D / 8), col = c % (D / 8);
+      kreg[i] = row < kvalid ? *reinterpret_cast<const u32x4*>(kb + row * krow + col * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg<D>::VCH; ++i)
+      vreg[i] = *reinterpret_cast<const u32x4*>(vb + (tid + kThreads * i) * 8);
+  }
+  __device__ void store(char* ks) const {
+    const int tid = threadIdx.x;
+    char* vs = ks + Cfg<D>::KBYTES;
+#pragma unroll
+    for (int i = 0; i < Cfg<D>::KCH; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / (D / 8), col = c % (D / 8);
+      *reinterpret_cast<u32x4*>(ks + row * Cfg<D>::KROWB + col * 16) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg<D>::VCH; ++i) {
+      const int c = tid + kThreads * i;
+      const int d = c / (BN / 8), col = c % (BN / 8);
+      *reinterpret_cast<u32x4*>(vs + d * VROWB + col * 16) = vreg[i];
+    }
+  }
+};
+
+// Per-wave flash state for 32 queries: O^T accumulators, running reference max
+// (log2 units) and this lane's partial row sum (keys it holds; the partner lane
+// l ^ 32 holds the rest of the query's keys).
+template <int D>
+struct Flash {
+  f32x16 o[Cfg<D>::DM];
+  float mrun, lsum;
+  __device__ void init() {
+#pragma unroll
+    for (int dm = 0; dm < Cfg<D>::DM; ++dm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dm][r] = 0.f;
+    mrun = -INFINITY;
+    lsum = 0.f;
+  }
+};
+
+// Load this lane's Q fragments (B operand of S^T = K Q^T) for query row qp (a pointer
+// to the row's d values, already offset by lh * 8), or zeros.
+template <int D>
+__device__ inline void load_q(const uint16_t* qp, bool ok, bf16x8 (&qf)[Cfg<D>::DK]) {
+#pragma unroll
+  for (int dk = 0; dk < Cfg<D>::DK; ++dk) {
+    u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(qp + dk * 16) : u32x4{0u, 0u, 0u, 0u};
+    qf[dk] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// One 64-key tile for this wave's 32 queries: S^T = K Q^T, hide keys kk > lim (kk =
+// key index inside the tile; lim >= 63 means no mask), online softmax in the log2
+// domain with a lazily raised reference, then O^T += V^T P^T.
+template <int D>
+__device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 (&qf)[Cfg<D>::DK],
+                                   Flash<D>& f, int lim, float c_log2) {
+  using C = Cfg<D>;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+  for (int dk = 0; dk < C::DK; ++dk) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + lr) * C::KROWB +
+                                                        (dk * 16 + lh * 8) * 2);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dk], s[kb], 0, 0, 0);
+    }
+  }
+  if (lim < BN - 1) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (kk > lim) s[kb][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mt = mx * c_log2;
+  if (__any(mt > f.mrun + kRescaleLog2)) {
+    const float mnew = fmaxf(f.mrun, mt);
+    const float alpha = __builtin_amdgcn_exp2f(f.mrun - (mnew == -INFINITY ? 0.f : mnew));
+    f.mrun = mnew;
+    f.lsum *= alpha;
+#pragma unroll
+    for (int dm = 0; dm < C::DM; ++dm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f.o[dm][r] *= alpha;
+  }
+  const float mref = f.mrun == -INFINITY ? 0.f : f.mrun;
+  bf16x8 pf[4];
+  float ps = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -mref));
+      s[kb][r] = pv;
+      ps += pv;
+    }
+  f.lsum += ps;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    const int kb = kc >> 1, half = kc & 1;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      f32x2 two = {s[kb][half * 8 + 2 * e2], s[kb][half * 8 + 2 * e2 + 1]};
+      bf16x2 cv = __builtin_convertvector(two, bf16x2);
+      pf[kc][2 * e2] = cv[0];
+      pf[kc][2 * e2 + 1] = cv[1];
+    }
+  }
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+    for (int dm = 0; dm < C::DM; ++dm) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (dm * 32 + lr) * VROWB +
+                                                        (kc * 16 + lh * 8) * 2);
+      f.o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], f.o[dm], 0, 0, 0);
+    }
+  }
+}
+
+// Final row sum of this lane's query (both lanes of the pair hold the same value).
+template <int D>
+__device__ inline float flash_rowsum(const Flash<D>& f) {
+  return f.lsum + __shfl_xor(f.lsum, 32);
+}
+
+// O[d] for this lane's query is f.o[dm][grp*4 + j] at d = dm*32 + 8*grp + 4*(l/32) + j.
+template <int D>
+__device__ inline int out_dim(int dm, int grp, int lh) {
+  return dm * 32 + 8 * grp + 4 * lh;
+}
+
+}  // namespace spava

@@ -1,0 +1,299 @@
+// Query block B_qr: per-host partial attention and log-sum-exp merge.
+//
+// Method (explainer "APB-V: ...", Methodik > Kontext-Splitting: the embeddings are
+// split into anchor, query block B_qr and context blocks; Systemseitige
+// Optimierungen > fused context + query forward: each host attends the query rows to
+// what it holds and the partial results are merged with FlashAttention's log-sum-exp
+// outputs). The partial key sets are disjoint — host h's own context block, plus the
+// query block's own keys (causal) — so the merge is exact: row i of B_qr sees every
+// context key and the query keys [0, i].
+//
+// Kernels:
+//   vt_rows    V^T tiles (MFMA slot order) of the context blocks and of the query keys;
+//   partial    bf16: one workgroup = 256 query rows x 1 head x 1 partial (H context
+//              blocks + the query block itself), the same flash step as the main
+//              attention; f32: one thread per query row, float32 VALU;
+//   merge      O = sum_h exp(LSE_h - LSE) O_h with LSE = log sum_h exp(LSE_h).
+#include "attn_common.h"
+
+namespace spava {
+namespace {
+
+// V^T tiles of `nsegs` consecutive segments of `nseg` rows of v (KV head = grid.y):
+// dst [Hkv][nsegs][tiles_per_seg][D][64]; rows past a segment's end are zero.
+// grid (nsegs * tiles_per_seg, Hkv), 256 threads.
+template <int D>
+__global__ __launch_bounds__(256) void vt_rows_kernel(const uint16_t* __restrict__ v, int64_t nseg,
+                                                      int nsegs, int tiles_per_seg,
+                                                      int64_t stride_tok, int64_t stride_head,
+                                                      uint16_t* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN][D + 8];
+  const int g = blockIdx.y;
+  const int seg = blockIdx.x / tiles_per_seg, tile = blockIdx.x % tiles_per_seg;
+  constexpr int CPR = D / 8;
+  for (int c = threadIdx.x; c < BN * CPR; c += 256) {
+    const int row = c / CPR, col = c % CPR;
+    const int64_t off = static_cast<int64_t>(tile) * BN + row;
+    uint4 vv = make_uint4(0, 0, 0, 0);
+    if (off < nseg)
+      vv = *reinterpret_cast<const uint4*>(v + (seg * nseg + off) * stride_tok + g * stride_head +
+                                           col * 8);
+    *reinterpret_cast<uint4*>(&Vs[row][col * 8]) = vv;
+  }
+  __syncthreads();
+  store_vt_tile<D>(Vs, dst + ((static_cast<int64_t>(g) * nsegs + seg) * tiles_per_seg + tile) *
+                                 D * BN);
+}
+
+// grid ((H + 1) * qtiles, Hq), kThreads threads. Partial ph < H: context block ph,
+// every key visible. Partial H: the query block's own keys, causal.
+template <int D>
+__global__ __launch_bounds__(kThreads) void query_partial_kernel(
+    Plan p, int64_t nq, int qtiles, const uint16_t* __restrict__ q_qr,
+    const uint16_t* __restrict__ k_qr, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ vtctx, const uint16_t* __restrict__ vtq,
+    float* __restrict__ part_o, float* __restrict__ part_lse, float c_log2) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  const int ph = blockIdx.x / qtiles, qt = blockIdx.x % qtiles;
+  const int hq = blockIdx.y, g = hq / p.G;
+  const bool self = ph == p.H;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int64_t q0 = static_cast<int64_t>(qt) * kQTile;
+  const int64_t qw0 = q0 + static_cast<int64_t>(kWaveQ) * w;
+  const int64_t qw_last = qw0 + kWaveQ - 1;
+  const int64_t qi = qw0 + lr;
+  const bool wave_active = qw0 < nq;
+
+  const int64_t s = static_cast<int64_t>(ph) * p.nb;   // context block start
+  const int qkt = static_cast<int>((nq + BN - 1) / BN);
+  const int ntiles = self ? static_cast<int>((min(nq, q0 + kQTile) + BN - 1) / BN) : p.loc_tiles;
+  const uint16_t* kbase = self ? k_qr + g * p.kvs_head : k + s * p.kvs_tok + g * p.kvs_head;
+  const int64_t nkeys = self ? nq : p.nb;
+  const uint16_t* vtbase = self ? vtq + static_cast<int64_t>(g) * qkt * D * BN
+                                : vtctx + (static_cast<int64_t>(g) * p.H + ph) * p.loc_tiles * D * BN;
+
+  TileStage<D> stage;
+  auto load_tile = [&](int it) {
+    const int64_t key0 = static_cast<int64_t>(it) * BN;
+    stage.load(kbase + key0 * p.kvs_tok, p.kvs_tok, nkeys - key0, vtbase + it * D * BN);
+  };
+
+  bf16x8 qf[C::DK];
+  load_q<D>(q_qr + qi * p.qs_tok + hq * p.qs_head + lh * 8, qi < nq, qf);
+  Flash<D> f;
+  f.init();
+
+  load_tile(0);
+  stage.store(smem);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) load_tile(it + 1);
+    const int64_t key0 = static_cast<int64_t>(it) * BN;
+    const bool skip = !wave_active || (self && key0 > qw_last);
+    if (!skip) {
+      // Hide keys past the segment end; in the query block also keys after the query.
+      int64_t lim = nkeys - key0 - 1;
+      if (self) lim = min(lim, qi - key0);
+      const char* ks = smem + (it & 1) * C::STAGE;
+      attend_tile<D>(ks, ks + C::KBYTES, qf, f, static_cast<int>(min<int64_t>(lim, BN - 1)), c_log2);
+    }
+    if (it + 1 < ntiles) stage.store(smem + ((it + 1) & 1) * C::STAGE);
+    __syncthreads();
+  }
+  const float ltot = flash_rowsum<D>(f);
+  if (qi < nq) {
+    const float inv = 1.f / ltot;
+    float* op = part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * D;
+#pragma unroll
+    for (int dm = 0; dm < C::DM; ++dm)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const float4 v4 = make_float4(f.o[dm][grp * 4] * inv, f.o[dm][grp * 4 + 1] * inv,
+                                      f.o[dm][grp * 4 + 2] * inv, f.o[dm][grp * 4 + 3] * inv);
+        *reinterpret_cast<float4*>(op + out_dim<D>(dm, grp, lh)) = v4;
+      }
+    if (lh == 0)
+      part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] =
+          (f.mrun + log2f(ltot)) * 0.69314718055994531f;
+  }
+}
+
+// float32 inputs: one thread per query row; grid ((H + 1) * ceil(nq / 64), Hq), 64 threads.
+template <int D>
+__global__ __launch_bounds__(64) void query_partial_f32_kernel(
+    Plan p, int64_t nq, int qtiles, const float* __restrict__ q_qr, const float* __restrict__ k_qr,
+    const float* __restrict__ v_qr, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ float Ks[BN][D + 1];
+  __shared__ float Vs[BN][D + 1];
+  const int ph = blockIdx.x / qtiles, qt = blockIdx.x % qtiles;
+  const int hq = blockIdx.y, g = hq / p.G;
+  const bool self = ph == p.H;
+  const int tid = threadIdx.x;
+  const int64_t qi = static_cast<int64_t>(qt) * BN + tid;
+  const bool valid = qi < nq;
+  const int64_t q_last = min(static_cast<int64_t>(qt + 1) * BN, nq) - 1;
+  const float scale = static_cast<float>(p.scale);
+  const float* kb = self ? k_qr : k + static_cast<int64_t>(ph) * p.nb * p.kvs_tok;
+  const float* vb = self ? v_qr : v + static_cast<int64_t>(ph) * p.nb * p.kvs_tok;
+  const int64_t nkeys = self ? q_last + 1 : p.nb;
+
+  float qr[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qr[d] = valid ? q_qr[qi * p.qs_tok + hq * p.qs_head + d] : 0.f;
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int64_t key0 = 0; key0 < nkeys; key0 += BN) {
+    __syncthreads();
+    for (int c = tid; c < BN * D; c += 64) {
+      const int row = c / D, d = c % D;
+      const int64_t key = key0 + row;
+      float kv = 0.f, vv = 0.f;
+      if (key < nkeys) {
+        kv = kb[key * p.kvs_tok + g * p.kvs_head + d];
+        vv = vb[key * p.kvs_tok + g * p.kvs_head + d];
+      }
+      Ks[row][d] = kv;
+      Vs[row][d] = vv;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < BN; ++kk) {
+      const int64_t key = key0 + kk;
+      const bool vis = key < nkeys && (!self || key <= qi);
+      if (!vis) continue;
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dot = fmaf(qr[d], Ks[kk][d], dot);
+      const float x = dot * scale;
+      if (x > m) {
+        const float alpha = expf(m - x);
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] *= alpha;
+        l *= alpha;
+        m = x;
+      }
+      const float pe = expf(x - m);
+      l += pe;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(pe, Vs[kk][d], acc[d]);
+    }
+  }
+  if (!valid) return;
+  const float inv = 1.f / l;
+  float* op = part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
+  part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] = m + logf(l);
+}
+
+__device__ inline void store4(uint16_t* dst, float4 v) {
+  f32x2 lo = {v.x, v.y}, hi = {v.z, v.w};
+  uint2 pk;
+  pk.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+  pk.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+  *reinterpret_cast<uint2*>(dst) = pk;
+}
+__device__ inline void store4(float* dst, float4 v) { *reinterpret_cast<float4*>(dst) = v; }
+
+// One thread per (row, head, 4 dims): LSE merge of the H + 1 partials.
+template <typename T>
+__global__ __launch_bounds__(256) void query_merge_kernel(Plan p, int64_t nq,
+                                                          const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse,
+                                                          T* __restrict__ out, float* __restrict__ lse) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int dq = p.D / 4;
+  if (t >= nq * p.Hq * dq) return;
+  const int d4 = static_cast<int>(t % dq);
+  const int64_t rh = t / dq;
+  const int hq = static_cast<int>(rh % p.Hq);
+  const int64_t qi = rh / p.Hq;
+  float m = -INFINITY;
+  for (int ph = 0; ph <= p.H; ++ph)
+    m = fmaxf(m, part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi]);
+  float ssum = 0.f;
+  for (int ph = 0; ph <= p.H; ++ph)
+    ssum += expf(part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] - m);
+  const float total = m + logf(ssum);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int ph = 0; ph <= p.H; ++ph) {
+    const float wgt = expf(part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] - total);
+    const float4 o = *reinterpret_cast<const float4*>(
+        part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * p.D + d4 * 4);
+    acc.x = fmaf(wgt, o.x, acc.x);
+    acc.y = fmaf(wgt, o.y, acc.y);
+    acc.z = fmaf(wgt, o.z, acc.z);
+    acc.w = fmaf(wgt, o.w, acc.w);
+  }
+  store4(out + qi * p.os_tok + hq * p.os_head + d4 * 4, acc);
+  if (lse && d4 == 0) lse[static_cast<int64_t>(hq) * nq + qi] = total;
+}
+
+template <int D>
+hipError_t launch_query_bf16(const Plan& p, int64_t nq, const uint16_t* q_qr, const uint16_t* k_qr,
+                             const uint16_t* v_qr, const uint16_t* k, const uint16_t* v,
+                             uint16_t* out, float* lse, char* ws, hipStream_t st) {
+  const QueryWs w = query_ws_layout(p, nq);
+  float* part_o = reinterpret_cast<float*>(ws + w.part_o);
+  float* part_lse = reinterpret_cast<float*>(ws + w.part_lse);
+  uint16_t* vtctx = reinterpret_cast<uint16_t*>(ws + w.vtctx);
+  uint16_t* vtq = reinterpret_cast<uint16_t*>(ws + w.vtq);
+  const int qkt = static_cast<int>(cdiv(nq, BN));
+  hipLaunchKernelGGL(vt_rows_kernel<D>, dim3(static_cast<unsigned>(p.H * p.loc_tiles), p.Hkv),
+                     dim3(256), 0, st, v, static_cast<int64_t>(p.nb), p.H, p.loc_tiles, p.kvs_tok,
+                     p.kvs_head, vtctx);
+  hipLaunchKernelGGL(vt_rows_kernel<D>, dim3(static_cast<unsigned>(qkt), p.Hkv), dim3(256), 0, st,
+                     v_qr, nq, 1, qkt, p.kvs_tok, p.kvs_head, vtq);
+  const int qtiles = static_cast<int>(cdiv(nq, kQTile));
+  const float c_log2 = static_cast<float>(p.scale * 1.4426950408889634);
+  hipLaunchKernelGGL(query_partial_kernel<D>, dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq),
+                     dim3(kThreads), 0, st, p, nq, qtiles, q_qr, k_qr, k, vtctx, vtq, part_o,
+                     part_lse, c_log2);
+  const int64_t threads = nq * p.Hq * (p.D / 4);
+  hipLaunchKernelGGL(query_merge_kernel<uint16_t>, dim3(static_cast<unsigned>(cdiv(threads, 256))),
+                     dim3(256), 0, st, p, nq, part_o, part_lse, out, lse);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_query_f32(const Plan& p, int64_t nq, const float* q_qr, const float* k_qr,
+                            const float* v_qr, const float* k, const float* v, float* out,
+                            float* lse, char* ws, hipStream_t st) {
+  const QueryWs w = query_ws_layout(p, nq);
+  float* part_o = reinterpret_cast<float*>(ws + w.part_o);
+  float* part_lse = reinterpret_cast<float*>(ws + w.part_lse);
+  const int qtiles = static_cast<int>(cdiv(nq, BN));
+  hipLaunchKernelGGL(query_partial_f32_kernel<D>,
+                     dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq), dim3(64), 0, st, p, nq,
+                     qtiles, q_qr, k_qr, v_qr, k, v, part_o, part_lse);
+  const int64_t threads = nq * p.Hq * (p.D / 4);
+  hipLaunchKernelGGL(query_merge_kernel<float>, dim3(static_cast<unsigned>(cdiv(threads, 256))),
+                     dim3(256), 0, st, p, nq, part_o, part_lse, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_query(const Plan& p, int64_t nq, const void* q_qr, const void* k_qr,
+                        const void* v_qr, const void* k, const void* v, void* out, float* lse,
+                        char* ws, hipStream_t st) {
+  if (p.dtype == SPAVA_BF16) {
+    auto c = [](const void* x) { return static_cast<const uint16_t*>(x); };
+    auto o = static_cast<uint16_t*>(out);
+    if (p.D == 128)
+      return launch_query_bf16<128>(p, nq, c(q_qr), c(k_qr), c(v_qr), c(k), c(v), o, lse, ws, st);
+    return launch_query_bf16<64>(p, nq, c(q_qr), c(k_qr), c(v_qr), c(k), c(v), o, lse, ws, st);
+  }
+  auto c = [](const void* x) { return static_cast<const float*>(x); };
+  auto o = static_cast<float*>(out);
+  if (p.D == 128)
+    return launch_query_f32<128>(p, nq, c(q_qr), c(k_qr), c(v_qr), c(k), c(v), o, lse, ws, st);
+  return launch_query_f32<64>(p, nq, c(q_qr), c(k_qr), c(v_qr), c(k), c(v), o, lse, ws, st);
+}
+
+}  // namespace spava

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/spava.h: argument checks, planning,
 // workspace carving and kernel launches. No device memory is allocated here.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -71,6 +72,13 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   p->KS = static_cast<int>(cdiv(nb, kScoreSplitKeys));
   p->T = static_cast<int>(cdiv(nb, kQTile));
   p->loc_tiles = static_cast<int>(cdiv(nb, kKeyTile));
+  // SPAVA_SCHEDULE=lpt|natural|zigzag picks the attention dispatch order (default:
+  // longest first). Every order computes the same values; only timing differs.
+  p->sched = kSchedLongestFirst;
+  if (const char* e = getenv("SPAVA_SCHEDULE")) {
+    if (strcmp(e, "natural") == 0) p->sched = kSchedNatural;
+    else if (strcmp(e, "zigzag") == 0) p->sched = kSchedZigZag;
+  }
   return SPAVA_OK;
 }
 
@@ -96,6 +104,19 @@ AttnWs attn_ws_layout(const Plan& p) {
                          : 0;
   w.vtloc = region(cur, loc);
   w.order = region(cur, static_cast<size_t>(p.H) * p.T * sizeof(int32_t));
+  w.total = cur;
+  return w;
+}
+
+QueryWs query_ws_layout(const Plan& p, int64_t nq) {
+  QueryWs w{};
+  size_t cur = 0;
+  const size_t parts = static_cast<size_t>(p.H + 1);
+  w.part_o = region(cur, parts * nq * p.Hq * p.D * sizeof(float));
+  w.part_lse = region(cur, parts * p.Hq * nq * sizeof(float));
+  const bool bf = p.dtype == SPAVA_BF16;
+  w.vtctx = region(cur, bf ? static_cast<size_t>(p.Hkv) * p.H * p.loc_tiles * kKeyTile * p.D * 2 : 0);
+  w.vtq = region(cur, bf ? static_cast<size_t>(p.Hkv) * cdiv(nq, kKeyTile) * kKeyTile * p.D * 2 : 0);
   w.total = cur;
   return w;
 }
@@ -214,6 +235,38 @@ spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, cons
   else
     e = launch_attn_f32(p, q, k, v, passing_idx, out, lse_out, static_cast<char*>(workspace),
                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
+}
+
+spava_status spava_query_workspace_bytes(const spava_shape* shape, int64_t n_query,
+                                         size_t* bytes) {
+  if (!bytes) return SPAVA_ERR_NULL;
+  Plan p;
+  spava_status st = make_plan(shape, &p);
+  if (st != SPAVA_OK) return st;
+  if (n_query < 1 || n_query > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
+  *bytes = query_ws_layout(p, n_query).total;
+  return SPAVA_OK;
+}
+
+spava_status spava_query_attn_fwd(const spava_shape* shape, int64_t n_query, const void* q_qr,
+                                  const void* k_qr, const void* v_qr, const void* k,
+                                  const void* v, void* out_qr, float* lse_qr, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Plan p;
+  spava_status st = make_plan(shape, &p);
+  if (st != SPAVA_OK) return st;
+  if (n_query < 1 || n_query > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
+  if (!q_qr || !k_qr || !v_qr || !k || !v || !out_qr || !workspace) return SPAVA_ERR_NULL;
+  if (!aligned16(q_qr) || !aligned16(k_qr) || !aligned16(v_qr) || !aligned16(k) ||
+      !aligned16(v) || !aligned16(out_qr) || !aligned16(workspace))
+    return SPAVA_ERR_ALIGN;
+  if (lse_qr && (reinterpret_cast<uintptr_t>(lse_qr) & 3u)) return SPAVA_ERR_ALIGN;
+  if (workspace_bytes < query_ws_layout(p, n_query).total) return SPAVA_ERR_WORKSPACE;
+  st = check_device();
+  if (st != SPAVA_OK) return st;
+  hipError_t e = launch_query(p, n_query, q_qr, k_qr, v_qr, k, v, out_qr, lse_qr,
+                              static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
 }
 

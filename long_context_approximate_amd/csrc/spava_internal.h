@@ -31,7 +31,11 @@ struct Plan {
   int KS;           // key splits of the row-statistics pass
   int T;            // query tiles per block
   int loc_tiles;    // key tiles per block
+  int sched;        // query-tile dispatch order (ScheduleMode); never changes results
 };
+
+// Dispatch order of the (block, query tile) pairs of the attention grid.
+enum ScheduleMode { kSchedLongestFirst = 0, kSchedNatural = 1, kSchedZigZag = 2 };
 
 // Non-local prefix length of block h: anchor + passing rows of blocks 0..h-1.
 __host__ __device__ inline int prefix_len(const Plan& p, int h) {
@@ -46,8 +50,13 @@ struct AttnWs {
   size_t kpre, vpre, vtloc, order, total;
 };
 
+struct QueryWs {
+  size_t part_o, part_lse, vtctx, vtq, total;
+};
+
 SelectWs select_ws_layout(const Plan& p);
 AttnWs attn_ws_layout(const Plan& p);
+QueryWs query_ws_layout(const Plan& p, int64_t nq);
 
 // Kernel launchers (defined next to their kernels). They return hipSuccess or the
 // launch error.
@@ -59,5 +68,8 @@ hipError_t launch_attn_bf16(const Plan& p, const void* q, const void* k, const v
 hipError_t launch_attn_f32(const Plan& p, const void* q, const void* k, const void* v,
                            const int32_t* idx, void* out, float* lse, char* ws,
                            hipStream_t st);
+hipError_t launch_query(const Plan& p, int64_t nq, const void* q_qr, const void* k_qr,
+                        const void* v_qr, const void* k, const void* v, void* out, float* lse,
+                        char* ws, hipStream_t st);
 
 }  // namespace spava

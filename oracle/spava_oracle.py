@@ -42,6 +42,9 @@ Readings where the pages are silent (each is listed in the design notes):
   R7 logits are scale * <q, k> with scale = 1/sqrt(d) unless given.
   R8 a query sees its own key (inclusive causal diagonal).
   R9 the last block's selection is never consumed and is not computed.
+  R17 the query block B_qr (text question, after the context) attends exactly to all
+     context keys and causally to its own keys; per-host partials over disjoint key
+     sets merged by log-sum-exp give exactly that (see query_block_attention).
 
 All arithmetic is float64 on the exact values of the stored inputs. Inputs may be
 passed as stored (bf16 bit patterns as uint16, or float32/float64); every function
@@ -290,3 +293,37 @@ def run(sh: Shape, q, k, v, attention: bool = True):
     if attention:
         out["o"], out["lse"] = approx_attention(sh, q, k, v, idx)
     return out
+
+
+# ------------------------------------------- query block B_qr (fused query forward)
+
+def query_block_attention(sh: Shape, q_qr, k_qr, v_qr, k, v):
+    """Attention of the query block B_qr: O [n_qr, Hq, d] and LSE [Hq, n_qr], float64.
+
+    [METH] Kontext-Splitting separates the text query block B_qr from the context
+    blocks; [SYS] fused context + query forward: every host attends the query rows to
+    what it holds and the partial results are merged with their log-sum-exp. Reading
+    (R17): the partial key sets are disjoint (each host's own context block, plus the
+    query's own keys), so the merge is exact: query row i sees every context key
+    [0, N) and the query keys [0, i] (causal). This function is that plain definition;
+    it does not split or merge.
+    """
+    n_qr = q_qr.shape[0]
+    G = sh.group
+    o = np.zeros((n_qr, sh.num_q_heads, sh.head_dim))
+    lse = np.zeros((sh.num_q_heads, n_qr))
+    rows = np.arange(n_qr)
+    for hq in range(sh.num_q_heads):
+        g = hq // G
+        kk = np.concatenate([to_f64(k[:, g, :]), to_f64(k_qr[:, g, :])])
+        vv = np.concatenate([to_f64(v[:, g, :]), to_f64(v_qr[:, g, :])])
+        x = sh.scale * (to_f64(q_qr[:, hq, :]) @ kk.T)             # [n_qr, N + n_qr]
+        hidden = np.zeros(x.shape, dtype=bool)
+        hidden[:, sh.seq_len:] = rows[None, :] > rows[:, None]     # causal inside B_qr
+        x = np.where(hidden, -np.inf, x)
+        m = x.max(axis=1, keepdims=True)
+        ex = np.exp(x - m)
+        z = ex.sum(axis=1, keepdims=True)
+        o[:, hq] = (ex / z) @ vv
+        lse[hq] = m[:, 0] + np.log(z[:, 0])
+    return o, lse

@@ -131,6 +131,25 @@ def test_calls_reject_bad_arguments_without_touching_the_gpu(lib):
     assert f(ctypes.byref(one), FAKE, FAKE, None, None, None, 0, None) == OK
 
 
+def test_query_entry_rejects_bad_arguments_without_touching_the_gpu(lib):
+    sh = _shape()
+    n = ctypes.c_size_t()
+    assert lib.spava_query_workspace_bytes(ctypes.byref(sh), 0, ctypes.byref(n)) == ERR_SHAPE
+    assert lib.spava_query_workspace_bytes(ctypes.byref(sh), 256, ctypes.byref(n)) == OK
+    # (H + 1) partial O and LSE in float32, then V^T tiles of the context and the query keys.
+    def r(b):
+        return (b + 255) // 256 * 256
+    expect = (r(5 * 256 * 8 * 128 * 4) + r(5 * 8 * 256 * 4) + r(2 * 4 * 16 * 64 * 128 * 2)
+              + r(2 * 4 * 64 * 128 * 2))
+    assert n.value == expect
+    f = lib.spava_query_attn_fwd
+    s = ctypes.byref(sh)
+    assert f(s, 256, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value, None) == ERR_NULL
+    assert f(s, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None, FAKE, n.value, None) == ERR_ALIGN
+    assert f(s, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value - 1, None) == ERR_WS
+    assert f(s, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value, None) == ERR_SHAPE
+
+
 def test_status_strings(lib):
     for code in range(8):
         assert spava.status_string(code).startswith("SPAVA")

@@ -209,3 +209,79 @@ def test_full_size_selection_and_sampled_rows(name):
     assert worst_o <= o_tol, f"max |dO| = {worst_o:.3e}"
     assert worst_l <= l_tol, f"max |dLSE| = {worst_l:.3e}"
     assert np.isfinite(got["out"]).all() and np.isfinite(got["lse"]).all()
+
+
+def test_schedules_give_identical_results(monkeypatch):
+    # The dispatch order (longest first, natural, ZigZag pairing) only changes timing.
+    cfg = small_config(name="sched", seq_len=4096, num_hosts=4, seed=26)
+    x = make_inputs(cfg)
+    results = {}
+    for mode in ("lpt", "natural", "zigzag"):
+        monkeypatch.setenv("SPAVA_SCHEDULE", mode)
+        results[mode], _ = _gpu_run(cfg, x)
+    for mode in ("natural", "zigzag"):
+        for key in ("idx", "out", "lse"):
+            assert np.array_equal(results[mode][key], results["lpt"][key]), (mode, key)
+
+
+# ------------------------------------------------------------- query block B_qr
+
+def _query_case(cfg, x, nq_take=None, context=None):
+    """Split stored inputs into context [0, N) and query block [N, N + nq)."""
+    n = cfg.seq_len if context is None else context
+    ctx = {name: arr[:n] for name, arr in x.items()}
+    qry = {name: arr[n:n + (nq_take or arr.shape[0] - n)] for name, arr in x.items()}
+    return ctx, qry
+
+
+def _gpu_query(cfg_ctx, ctx, qry):
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    d_ctx = spava.device_tensors(ctx, "cuda")
+    d_qry = spava.device_tensors(qry, "cuda")
+    shape = spava.shape_from_config(cfg_ctx)
+    nq = qry["q"].shape[0]
+    out = torch.full((nq, cfg_ctx.num_q_heads, cfg_ctx.head_dim), float("nan"),
+                     dtype=d_qry["q"].dtype, device="cuda")
+    lse = torch.full((cfg_ctx.num_q_heads, nq), float("nan"), dtype=torch.float32, device="cuda")
+    spava.spava_query_attn_fwd(shape, d_qry["q"], d_qry["k"], d_qry["v"], d_ctx["k"], d_ctx["v"],
+                               out, lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+QUERY = [
+    (small_config(name="qb_bf16", seq_len=3000 + 300, num_hosts=3, seed=41), 3000),
+    (small_config(name="qb_bf16_d64", head_dim=64, seq_len=2048 + 64, num_hosts=4, seed=42), 2048),
+    (small_config(name="qb_f32", dtype="f32", seq_len=1200 + 37, num_hosts=4, seed=43), 1200),
+    (small_config(name="qb_f32_d64", dtype="f32", head_dim=64, seq_len=512 + 16, num_hosts=2,
+                  num_q_heads=2, num_kv_heads=2, seed=44), 512),
+    (small_config(name="qb_one_host", seq_len=1000 + 257, num_hosts=1, anchor_len=0, seed=45), 1000),
+]
+
+
+@pytest.mark.parametrize("cfg,n_ctx", QUERY, ids=[c.name for c, _ in QUERY])
+def test_query_block_parity(cfg, n_ctx):
+    x = make_inputs(cfg)
+    ctx, qry = _query_case(cfg, x, context=n_ctx)
+    cfg_ctx = cfg.with_(seq_len=n_ctx)
+    out, lse = _gpu_query(cfg_ctx, ctx, qry)
+    ro, rl = oracle.query_block_attention(oracle.shape_of(cfg_ctx), qry["q"], qry["k"], qry["v"],
+                                          ctx["k"], ctx["v"])
+    o_tol, l_tol = TOL[cfg.dtype]
+    assert np.abs(out - ro).max() <= o_tol
+    assert np.abs(lse - rl).max() <= l_tol
+
+
+def test_query_block_video_workload():
+    # The 64K video workload: 65280 video tokens of context (H = 8 blocks of 8160) and
+    # the 256 trailing text tokens as the query block.
+    cfg = CONFIGS["video_h8_64k"]
+    x = make_inputs(cfg)
+    ctx, qry = _query_case(cfg, x, context=65280)
+    cfg_ctx = cfg.with_(seq_len=65280)
+    out, lse = _gpu_query(cfg_ctx, ctx, qry)
+    ro, rl = oracle.query_block_attention(oracle.shape_of(cfg_ctx), qry["q"], qry["k"], qry["v"],
+                                          ctx["k"], ctx["v"])
+    assert np.abs(out - ro).max() <= 2e-2
+    assert np.abs(lse - rl).max() <= 1e-3

@@ -309,3 +309,21 @@ def test_passing_lengths_clip_to_candidates():
     q, k, _ = _qkv(sh, rng)
     idx = orc.select_passing(sh, orc.all_window_scores(sh, q, k))
     assert np.all(idx[0] == -1)
+
+
+def test_query_block_is_the_tail_of_dense_causal_attention():
+    # B_qr appended after the context: its rows of a dense causal attention over
+    # [context ; query] see every context key and the earlier query keys (library pin).
+    rng = np.random.default_rng(31)
+    sh = orc.Shape(60, 3, 4, 2, 16, 4, 5, 3)
+    q, k, v = _qkv(sh, rng)
+    nq = 9
+    q_qr, k_qr, v_qr = (_bf16_exact((nq, 4, 16), rng), _bf16_exact((nq, 2, 16), rng),
+                        _bf16_exact((nq, 2, 16), rng))
+    o, lse = orc.query_block_attention(sh, q_qr, k_qr, v_qr, k, v)
+    cat = orc.Shape(60 + nq, 1, 4, 2, 16, 0, 0, 1)
+    qc = np.concatenate([q, q_qr]); kc = np.concatenate([k, k_qr]); vc = np.concatenate([v, v_qr])
+    ref = _sdpa(qc, kc, vc, cat, causal=True)[60:]
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    tri = np.tril(np.ones((60 + nq, 60 + nq), dtype=bool))
+    np.testing.assert_allclose(lse, _causal_lse(qc, kc, cat, tri)[:, 60:], rtol=0, atol=1e-12)
