@@ -163,6 +163,27 @@ spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, cons
                                    float* lse_out, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Bytes of workspace spava_select_passing_query needs (host only). */
+spava_status spava_select_query_workspace_bytes(const spava_shape* shape, int64_t n_query,
+                                                size_t* bytes);
+
+/*
+ * Query-aware passing-block selection (a variant of spava_select_passing; explainer
+ * "APB-V: ...", Methodik > Passing Blocks: KV rows ranked by query-to-context
+ * attention scores). The observers are the n_query rows of the query block q_qr
+ * (all G query heads of each KV group) instead of each block's last w queries; the
+ * query block follows the whole context, so every key of block j is visible:
+ *   score_j,g(p) = mean over hq in g and rows i of q_qr of
+ *                  softmax over p' in block j of (sm_scale * <q_qr_i, k_p'>), at p.
+ * Selection, output layout, tie rule and errors are those of spava_select_passing;
+ * `window` is not used. q_qr is [n_query, Hq, d] with the shape's q strides;
+ * 1 <= n_query and n_query * G <= 2^30.
+ */
+spava_status spava_select_passing_query(const spava_shape* shape, int64_t n_query,
+                                        const void* q_qr, const void* k, int32_t* passing_idx,
+                                        double* scores_out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace spava_query_attn_fwd needs for n_query query rows (host only). */
 spava_status spava_query_workspace_bytes(const spava_shape* shape, int64_t n_query,
                                          size_t* bytes);

@@ -8,6 +8,9 @@
 // causal keys [s_j, i]. Selection takes the l_j largest, ties to the lower position.
 //
 // Kernels, in launch order:
+// Observers are the last w queries of each block (causal), or, for the query-aware
+// variant, the rows of a query block that follows the context (every key visible).
+//
 //   rowstats  (m, z) = (max logit, sum exp(logit - max)) of every observer row over
 //             one key split; float64 dot products on v_mfma_f64_16x16x4_f64;
 //   merge     combine the key splits of each row into (m, 1/z);
@@ -86,9 +89,15 @@ __device__ inline void opaque(F& f) {
   for (int i = 0; i < F::W; ++i) asm volatile("" : "+v"(f.w[i]));
 }
 
-// Observer row r of (block j, KV head g): head g*G + r / w, query e_j - w + r % w.
+// Observer row r of (block j, KV head g): head g*G + r / w and query row e_j - w + r % w
+// of q, or row r % w of the query block when the observers are the query block.
 __device__ inline int64_t row_token(const Plan& p, int j, int r) {
-  return static_cast<int64_t>(j + 1) * p.nb - p.w + (r % p.w);
+  return p.obs_query ? (r % p.w) : static_cast<int64_t>(j + 1) * p.nb - p.w + (r % p.w);
+}
+// Last key position observer row r sees: its own position (causal), or every key of
+// the block for query-block observers.
+__device__ inline int64_t row_key_limit(const Plan& p, int j, int r) {
+  return p.obs_query ? INT64_MAX : row_token(p, j, r);
 }
 __device__ inline int row_head(const Plan& p, int g, int r) { return g * p.G + r / p.w; }
 
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
       m[rb][rr] = -INFINITY;
       z[rb][rr] = 0.0;
       const int r = r0 + rb * 16 + 4 * rr + kg;
-      qi[rb][rr] = r < p.R ? row_token(p, j, r) : -1;   // -1: padding row sees nothing
+      qi[rb][rr] = r < p.R ? row_key_limit(p, j, r) : -1;   // -1: padding row sees nothing
     }
   Frag<T, D> kf[2];
   load_keys<T, D>(p, k, g, split_lo, split_hi, col, kg, kf);
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(256) void colsum_kernel(Plan p, const T* __restrict
         const int r = r0 + rb * 16 + 4 * rr + kg;
         const bool ok = r < p.R;
         const double2 mz = ok ? st[r] : make_double2(0.0, 0.0);
-        const int64_t qi = ok ? row_token(p, j, r) : -1;
+        const int64_t qi = ok ? row_key_limit(p, j, r) : -1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const double x = p.scale * acc[rb][kb][rr];

@@ -74,6 +74,7 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   p->loc_tiles = static_cast<int>(cdiv(nb, kKeyTile));
   // SPAVA_SCHEDULE=lpt|natural|zigzag picks the attention dispatch order (default:
   // longest first). Every order computes the same values; only timing differs.
+  p->obs_query = 0;
   p->sched = kSchedLongestFirst;
   if (const char* e = getenv("SPAVA_SCHEDULE")) {
     if (strcmp(e, "natural") == 0) p->sched = kSchedNatural;
@@ -235,6 +236,54 @@ spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, cons
   else
     e = launch_attn_f32(p, q, k, v, passing_idx, out, lse_out, static_cast<char*>(workspace),
                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
+}
+
+// Plan of the query-aware selection: observers are the n_query rows of a query block.
+static spava_status make_query_select_plan(const spava_shape* shape, int64_t n_query, Plan* p) {
+  spava_status st = make_plan(shape, p);
+  if (st != SPAVA_OK) return st;
+  if (n_query < 1 || n_query * p->G > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
+  p->w = static_cast<int>(n_query);
+  p->R = static_cast<int>(n_query * p->G);
+  p->obs_query = 1;
+  return SPAVA_OK;
+}
+
+spava_status spava_select_query_workspace_bytes(const spava_shape* shape, int64_t n_query,
+                                                size_t* bytes) {
+  if (!bytes) return SPAVA_ERR_NULL;
+  Plan p;
+  spava_status st = make_query_select_plan(shape, n_query, &p);
+  if (st != SPAVA_OK) return st;
+  *bytes = select_ws_layout(p).total;
+  return SPAVA_OK;
+}
+
+spava_status spava_select_passing_query(const spava_shape* shape, int64_t n_query,
+                                        const void* q_qr, const void* k, int32_t* passing_idx,
+                                        double* scores_out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  Plan p;
+  spava_status st = make_query_select_plan(shape, n_query, &p);
+  if (st != SPAVA_OK) return st;
+  if (!q_qr || !k) return SPAVA_ERR_NULL;
+  const bool any = p.H > 1 && p.l > 0;
+  if (any && !passing_idx) return SPAVA_ERR_NULL;
+  if (!aligned16(q_qr) || !aligned16(k)) return SPAVA_ERR_ALIGN;
+  if (passing_idx && (reinterpret_cast<uintptr_t>(passing_idx) & 3u)) return SPAVA_ERR_ALIGN;
+  if (scores_out && (reinterpret_cast<uintptr_t>(scores_out) & 7u)) return SPAVA_ERR_ALIGN;
+  const SelectWs ws = select_ws_layout(p);
+  if (p.H > 1 && (any || scores_out)) {
+    if (!workspace) return SPAVA_ERR_NULL;
+    if (!aligned16(workspace)) return SPAVA_ERR_ALIGN;
+    if (workspace_bytes < ws.total) return SPAVA_ERR_WORKSPACE;
+  }
+  if (p.H == 1 || (!any && !scores_out)) return SPAVA_OK;
+  st = check_device();
+  if (st != SPAVA_OK) return st;
+  hipError_t e = launch_select(p, q_qr, k, passing_idx, scores_out, static_cast<char*>(workspace),
+                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
 }
 

@@ -32,6 +32,8 @@ struct Plan {
   int T;            // query tiles per block
   int loc_tiles;    // key tiles per block
   int sched;        // query-tile dispatch order (ScheduleMode); never changes results
+  int obs_query;    // selection observers: 0 = last w queries of each block,
+                    // 1 = the w rows of a query block (every key visible)
 };
 
 // Dispatch order of the (block, query tile) pairs of the attention grid.

@@ -28,6 +28,8 @@ EXPORTS = (
     "spava_approx_attn_fwd",
     "spava_query_workspace_bytes",
     "spava_query_attn_fwd",
+    "spava_select_query_workspace_bytes",
+    "spava_select_passing_query",
 )
 
 
@@ -94,6 +96,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.spava_query_attn_fwd.argtypes = [shp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, f32p, vp, sz,
                                          vp]
     lib.spava_query_attn_fwd.restype = ctypes.c_int
+    lib.spava_select_query_workspace_bytes.argtypes = [shp, ctypes.c_int64,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.spava_select_query_workspace_bytes.restype = ctypes.c_int
+    lib.spava_select_passing_query.argtypes = [shp, ctypes.c_int64, vp, vp, i32p, f64p, vp, sz, vp]
+    lib.spava_select_passing_query.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -176,6 +183,25 @@ def spava_approx_attn_fwd(shape: SpavaShape, q, k, v, passing_idx, out, lse_out=
     _check(load().spava_approx_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                         _ptr(passing_idx), _ptr(out), _ptr(lse_out), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)))
+    return ws
+
+
+def spava_select_query_workspace_bytes(shape: SpavaShape, n_query: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().spava_select_query_workspace_bytes(ctypes.byref(shape), n_query,
+                                                     ctypes.byref(n)))
+    return n.value
+
+
+def spava_select_passing_query(shape: SpavaShape, q_qr, k, passing_idx, scores_out=None,
+                               workspace=None, stream=None):
+    """Query-aware selection: observers are the rows of q_qr ([n_query, Hq, d])."""
+    n_query = q_qr.shape[0]
+    nbytes = spava_select_query_workspace_bytes(shape, n_query)
+    ws = _workspace(nbytes, q_qr.device, workspace)
+    _check(load().spava_select_passing_query(ctypes.byref(shape), n_query, _ptr(q_qr), _ptr(k),
+                                             _ptr(passing_idx), _ptr(scores_out), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)))
     return ws
 
 

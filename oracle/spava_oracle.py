@@ -45,6 +45,9 @@ Readings where the pages are silent (each is listed in the design notes):
   R17 the query block B_qr (text question, after the context) attends exactly to all
      context keys and causally to its own keys; per-host partials over disjoint key
      sets merged by log-sum-exp give exactly that (see query_block_attention).
+  R18 (variant) query-aware selection: the observers scoring a block's keys are the
+     query block's rows (all G heads), over all of the block's keys; selection rule
+     as in R5 (see query_window_scores).
 
 All arithmetic is float64 on the exact values of the stored inputs. Inputs may be
 passed as stored (bf16 bit patterns as uint16, or float32/float64); every function
@@ -327,3 +330,37 @@ def query_block_attention(sh: Shape, q_qr, k_qr, v_qr, k, v):
         o[:, hq] = (ex / z) @ vv
         lse[hq] = m[:, 0] + np.log(z[:, 0])
     return o, lse
+
+
+# ------------------------------------------- query-aware passing selection (variant)
+
+def query_window_scores(sh: Shape, q_qr, k, j: int, g: int) -> np.ndarray:
+    """Importance of every key of block j for KV head g, scored by the query block.
+
+    [METH] Passing Blocks: KV rows are ranked by query-to-context attention scores.
+    Reading R18 (variant): the observers are the rows of the query block B_qr (all G
+    query heads of group g) instead of the block's last w queries. B_qr follows the
+    whole context, so every key of block j is visible; each observer's softmax runs
+    over block j's keys, and the score is the mean probability mass. float64 [n_b].
+    """
+    s, e = context_block(sh, j)
+    G = sh.group
+    n_qr = q_qr.shape[0]
+    kl = to_f64(k[s:e, g, :])
+    total = np.zeros(e - s, dtype=np.float64)
+    for hq in range(g * G, (g + 1) * G):
+        x = sh.scale * (to_f64(q_qr[:, hq, :]) @ kl.T)               # [n_qr, n_b]
+        m = x.max(axis=1, keepdims=True)
+        ex = np.exp(x - m)
+        total += (ex / ex.sum(axis=1, keepdims=True)).sum(axis=0)
+    return total / (G * n_qr)
+
+
+def all_query_scores(sh: Shape, q_qr, k) -> np.ndarray:
+    """Query-aware scores of every block that passes rows: float64 [H-1, Hkv, n_b]."""
+    H, hkv, nb = sh.num_hosts, sh.num_kv_heads, sh.block_len
+    out = np.zeros((max(H - 1, 0), hkv, nb), dtype=np.float64)
+    for j in range(H - 1):
+        for g in range(hkv):
+            out[j, g] = query_window_scores(sh, q_qr, k, j, g)
+    return out

@@ -150,6 +150,24 @@ def test_query_entry_rejects_bad_arguments_without_touching_the_gpu(lib):
     assert f(s, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value, None) == ERR_SHAPE
 
 
+def test_query_selection_entry_validation(lib):
+    sh = _shape()
+    n = ctypes.c_size_t()
+    assert lib.spava_select_query_workspace_bytes(ctypes.byref(sh), 0, ctypes.byref(n)) == ERR_SHAPE
+    assert lib.spava_select_query_workspace_bytes(ctypes.byref(sh), 100, ctypes.byref(n)) == OK
+    # Same layout as the window variant with w = n_query observers per head.
+    def r(b):
+        return (b + 255) // 256 * 256
+    jg, R = 3 * 2, 4 * 100
+    assert n.value == r(jg * 1 * R * 16) + r(jg * R * 16) + r(jg * 1024 * 8)
+    f = lib.spava_select_passing_query
+    s = ctypes.byref(sh)
+    assert f(s, 100, None, FAKE, FAKE, None, FAKE, n.value, None) == ERR_NULL
+    assert f(s, 100, FAKE, FAKE, None, None, FAKE, n.value, None) == ERR_NULL
+    assert f(s, 100, FAKE, FAKE + 2, FAKE, None, FAKE, n.value, None) == ERR_ALIGN
+    assert f(s, 100, FAKE, FAKE, FAKE, None, FAKE, n.value - 1, None) == ERR_WS
+
+
 def test_status_strings(lib):
     for code in range(8):
         assert spava.status_string(code).startswith("SPAVA")

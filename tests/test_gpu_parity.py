@@ -285,3 +285,51 @@ def test_query_block_video_workload():
                                           ctx["k"], ctx["v"])
     assert np.abs(out - ro).max() <= 2e-2
     assert np.abs(lse - rl).max() <= 1e-3
+
+
+# ------------------------------------------------- query-aware selection variant
+
+def _gpu_query_select(cfg, x, q_qr):
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    dev = spava.device_tensors({"k": x["k"], "q_qr": q_qr}, "cuda")
+    shape = spava.shape_from_config(cfg)
+    H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
+    idx = torch.full((max(H - 1, 0), hkv, l), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((max(H - 1, 0), hkv, nb), -1.0, dtype=torch.float64, device="cuda")
+    spava.spava_select_passing_query(shape, dev["q_qr"], dev["k"], idx, sc)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+QSEL = [
+    (small_config(name="qsel_bf16", seq_len=3000, num_hosts=3, seed=51), 37),
+    (small_config(name="qsel_f32", dtype="f32", seq_len=1200, num_hosts=4, seed=52), 5),
+    (small_config(name="qsel_d64_many", head_dim=64, seq_len=2048, num_hosts=4, seed=53), 300),
+    (CONFIGS["h8_128k"], 256),
+]
+
+
+@pytest.mark.parametrize("cfg,nq", QSEL, ids=[c.name for c, _ in QSEL])
+def test_query_aware_selection_parity(cfg, nq):
+    x = make_inputs(cfg)
+    # A query block drawn from its own seed, with the workload's head layout.
+    qcfg = cfg.with_(seq_len=nq, num_hosts=1, anchor_len=0, window=1, seed=cfg.seed + 500)
+    q_qr = make_inputs(qcfg)["q"]
+    idx, sc = _gpu_query_select(cfg, x, q_qr)
+    sh = oracle.shape_of(cfg)
+    ref_sc = oracle.all_query_scores(sh, q_qr, x["k"])
+    ref_idx = oracle.select_passing(sh, ref_sc)
+    _check_selection(cfg, {"idx": idx, "scores": sc}, {"idx": ref_idx, "scores": ref_sc})
+
+
+def test_query_aware_ties_go_to_lower_positions():
+    cfg = small_config(name="qsel_ties", seq_len=1536, num_hosts=3, seed=54)
+    x = make_inputs(cfg)
+    q_qr = np.zeros((16, cfg.num_q_heads, cfg.head_dim), dtype=np.uint16)   # all logits 0
+    idx, _ = _gpu_query_select(cfg, x, q_qr)
+    sh = oracle.shape_of(cfg)
+    for j in range(cfg.num_hosts - 1):
+        cand = oracle.passing_candidates(sh, j)
+        for g in range(cfg.num_kv_heads):
+            assert list(idx[j, g]) == list(cand[:cfg.passing_len])

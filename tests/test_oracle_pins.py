@@ -327,3 +327,41 @@ def test_query_block_is_the_tail_of_dense_causal_attention():
     np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
     tri = np.tril(np.ones((60 + nq, 60 + nq), dtype=bool))
     np.testing.assert_allclose(lse, _causal_lse(qc, kc, cat, tri)[:, 60:], rtol=0, atol=1e-12)
+
+
+def test_query_aware_scores_decimal_bruteforce_and_invariants():
+    rng = np.random.default_rng(33)
+    sh = orc.Shape(24, 3, 4, 2, 8, 2, 3, 3)
+    _, k, _ = _qkv(sh, rng)
+    q_qr = _bf16_exact((5, 4, 8), rng)
+    getcontext().prec = 40
+    scores = orc.all_query_scores(sh, q_qr, k)
+    np.testing.assert_allclose(scores.sum(axis=2), 1.0, rtol=0, atol=1e-14)
+    for j in range(2):
+        s, e = orc.context_block(sh, j)
+        for g in range(2):
+            total = [Decimal(0)] * (e - s)
+            for hq in range(2 * g, 2 * g + 2):
+                for i in range(5):
+                    xs = [Decimal(sh.scale) * sum(Decimal(float(a)) * Decimal(float(b))
+                                                  for a, b in zip(q_qr[i, hq], k[p, g]))
+                          for p in range(s, e)]
+                    m = max(xs)
+                    ex = [(x - m).exp() for x in xs]
+                    z = sum(ex)
+                    for t, val in enumerate(ex):
+                        total[t] += val / z
+            ref = [float(t / 10) for t in total]
+            np.testing.assert_allclose(scores[j, g], ref, rtol=1e-13, atol=0)
+
+
+def test_query_aware_scores_equal_window_scores_of_a_last_row_observer():
+    # One observer equal to block j's last query sees every key of the block under the
+    # causal rule too, so the two scorings coincide (w = 1, G = 1).
+    rng = np.random.default_rng(34)
+    sh = orc.Shape(64, 2, 2, 2, 16, 3, 5, 1)
+    q, k, _ = _qkv(sh, rng)
+    win = orc.all_window_scores(sh, q, k)
+    q_qr = q[31:32].copy()                     # block 0 ends at 32
+    qa = orc.all_query_scores(sh, q_qr, k)
+    np.testing.assert_allclose(qa, win, rtol=1e-15, atol=0)
