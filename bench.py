@@ -170,6 +170,31 @@ def dense_baseline(cfg, q, k, v, stream, t_step, reps=3):
             "approx_step_speedup": ms / (t_step * 1e3)}
 
 
+def query_block_timing(cfg, shape, k, v, stream, n_query=256, reps=5):
+    """A 256-row query block after the context: its exact attention (H + 1 partials +
+    log-sum-exp merge) and the query-aware passing selection, on this workload."""
+    import torch
+
+    from long_context_approximate_amd import spava
+    from long_context_approximate_amd.inputs import make_inputs
+    qcfg = cfg.with_(seq_len=n_query, num_hosts=1, anchor_len=0, window=1, seed=cfg.seed + 500)
+    qd = spava.device_tensors(make_inputs(qcfg), "cuda:0")
+    out = torch.empty_like(qd["q"])
+    ws_q = torch.empty(spava.spava_query_workspace_bytes(shape, n_query), dtype=torch.uint8,
+                       device="cuda")
+    attn_ms = _time_call(lambda: spava.spava_query_attn_fwd(shape, qd["q"], qd["k"], qd["v"], k, v,
+                                                            out, None, ws_q, stream), stream, reps)
+    H, hkv, l = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len
+    idx = torch.empty((max(H - 1, 0), hkv, l), dtype=torch.int32, device="cuda")
+    ws_s = torch.empty(max(spava.spava_select_query_workspace_bytes(shape, n_query), 1),
+                       dtype=torch.uint8, device="cuda")
+    sel_ms = _time_call(lambda: spava.spava_select_passing_query(shape, qd["q"], k, idx, None,
+                                                                 ws_s, stream), stream, reps)
+    flops = 4.0 * cfg.head_dim * cfg.num_q_heads * n_query * (cfg.seq_len + (n_query + 1) / 2)
+    return {"n_query": n_query, "attn_ms": attn_ms, "attn_tflops": flops / attn_ms / 1e9,
+            "query_aware_select_ms": sel_ms}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +296,7 @@ def main():
     if not args.no_extras:
         rec["schedules_attn_ms"] = time_schedules(shape, q, k, v, idx, out, lse, ws_attn, stream)
         rec["dense_causal"] = dense_baseline(cfg, q, k, v, stream, t_step)
+        rec["query_block"] = query_block_timing(cfg, shape, k, v, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, x)
     print(json.dumps(rec), flush=True)

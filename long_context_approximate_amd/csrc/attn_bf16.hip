@@ -204,7 +204,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     // accumulators in place across iterations.
     int lim = BN - 1;
     if (!local && it == npre - 1 && (L % BN) != 0) lim = L - it * BN - 1;
-    if (local && key0 + BN - 1 > qw0) lim = static_cast<int>(max<int64_t>(qi - key0, -1));
+    if (local && key0 + BN - 1 > qw0) {
+      const int64_t rel = qi - key0;               // integer select (no floating max)
+      lim = rel < 0 ? -1 : static_cast<int>(rel);
+    }
     if (!wave_active) lim = -1;
     const char* ks = smem + (it & 1) * C::STAGE;
     attend_tile<D>(ks, ks + C::KBYTES, qf, f, lim, c_log2);
