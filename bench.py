@@ -28,7 +28,8 @@ if ROOT not in sys.path:
 METRIC = "approx-attn prefill tokens/s + TFLOP/s (% bf16 MFMA peak), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_h8_128k_pmc.json")
-ATTN_SOURCE = os.path.join(ROOT, "long_context_approximate_amd", "csrc", "attn_bf16.hip")
+ATTN_SOURCES = [os.path.join(ROOT, "long_context_approximate_amd", "csrc", f)
+                for f in ("attn_bf16.hip", "attn_common.h")]
 
 
 def key_visits_per_head(cfg) -> int:
@@ -47,13 +48,20 @@ def attn_flops(cfg) -> float:
     return 4.0 * cfg.head_dim * cfg.num_q_heads * key_visits_per_head(cfg)
 
 
+def attn_sources_sha256() -> str:
+    """Hash of the attention kernel's source files (the counters are tied to it)."""
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_from_profile():
     """HBM bytes per attention launch from the committed rocprofv3 PMC summary, or None
     when the summary is missing or the kernel source changed since it was taken."""
     try:
         rec = json.load(open(PMC_SUMMARY))
-        src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-        if rec.get("attn_bf16_sha256") != src:
+        if rec.get("attn_sources_sha256") != attn_sources_sha256():
             return None
         return float(rec["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):

@@ -27,11 +27,16 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kWaveQ = 32;                    // queries per wave
 static_assert(kWaves * kWaveQ == kQTile, "query tile must match the plan");
 
-// Softmax rescale threshold (log2 units): the running reference max is only raised
-// when a tile's max exceeds it by more than this, so exp2 values stay <= 2^8 and the
-// accumulators are rescaled rarely. The result is exact: numerator and denominator
-// share the reference.
-constexpr float kRescaleLog2 = 8.0f;
+// Softmax reference (log2 units). p = exp2(c*s - ref) is computed against the running
+// reference first; only when a lane's partial tile sum leaves [0, kSumLimit] (a logit
+// about 8 or more above the reference, or the first unmasked tile) is the reference
+// raised to the tile maximum, O and the row sum rescaled and the tile recomputed. So
+// the per-tile maximum is never needed on the common path. The result is exact:
+// numerator and denominator share the reference. Raising the reference to a new
+// dominant logit keeps that key's weight at exactly 1, free of bf16 rounding in P.
+// kRefInit is finite so that masked scores (-inf) give p = 0 and never NaN.
+constexpr float kRefInit = -1.0e30f;
+constexpr float kSumLimit = 256.0f;
 
 template <int D>
 struct Cfg {
@@ -122,7 +127,7 @@ struct Flash {
     for (int dm = 0; dm < Cfg<D>::DM; ++dm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dm][r] = 0.f;
-    mrun = -INFINITY;
+    mrun = kRefInit;
     lsum = 0.f;
   }
 };
@@ -138,29 +143,69 @@ __device__ inline void load_q(const uint16_t* qp, bool ok, bf16x8 (&qf)[Cfg<D>::
   }
 }
 
+// p = exp2(c*s - ref) of this lane's 32 scores, packed to bf16 in the P^T operand
+// order; returns the lane's partial sum of the float32 values.
+__device__ inline float exp_tile(const f32x16 (&s)[2], float ref, float c_log2, bf16x8 (&pf)[4]) {
+  float sum0 = 0.f, sum1 = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    const int kb = kc >> 1, half = kc & 1;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int r = half * 8 + 2 * e2;
+      f32x2 two = {__builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -ref)),
+                   __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c_log2, -ref))};
+      if (kc & 1) sum1 += two[0] + two[1];
+      else sum0 += two[0] + two[1];
+      const bf16x2 cv = __builtin_convertvector(two, bf16x2);
+      pf[kc][2 * e2] = cv[0];
+      pf[kc][2 * e2 + 1] = cv[1];
+    }
+  }
+  return sum0 + sum1;
+}
+
 // One 64-key tile for this wave's 32 queries: S^T = K Q^T, hide keys kk > lim (kk =
 // key index inside the tile; lim >= 63 means no mask), online softmax in the log2
-// domain with a lazily raised reference, then O^T += V^T P^T.
+// domain against the running reference, then O^T += V^T P^T. LDS fragments are read
+// in batches ahead of their products (all K fragments first; V^T fragments in two
+// halves), so each batch is in flight while earlier work runs.
 template <int D>
 __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 (&qf)[Cfg<D>::DK],
                                    Flash<D>& f, int lim, float c_log2) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
+  bf16x8 kf[2 * C::DK];
+#pragma unroll
+  for (int dk = 0; dk < C::DK; ++dk)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      kf[dk * 2 + kb] = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + lr) * C::KROWB +
+                                                        (dk * 16 + lh * 8) * 2);
+  __builtin_amdgcn_sched_barrier(0);
   f32x16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-  for (int dk = 0; dk < C::DK; ++dk) {
+  for (int dk = 0; dk < C::DK; ++dk)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + lr) * C::KROWB +
-                                                        (dk * 16 + lh * 8) * 2);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dk], s[kb], 0, 0, 0);
-    }
-  }
+    for (int kb = 0; kb < 2; ++kb)
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk * 2 + kb], qf[dk], s[kb], 0, 0, 0);
+  // V^T fragments of key chunks 0-1 now (in flight during the softmax), of chunks 2-3
+  // once the first half of the products is issued.
+  bf16x8 vf[4 * C::DM];
+  auto read_v = [&](int kc) {
+#pragma unroll
+    for (int dm = 0; dm < C::DM; ++dm)
+      vf[kc * C::DM + dm] = *reinterpret_cast<const bf16x8*>(vs + (dm * 32 + lr) * VROWB +
+                                                            (kc * 16 + lh * 8) * 2);
+  };
+  read_v(0);
+  read_v(1);
+  __builtin_amdgcn_sched_barrier(0);
   if (lim < BN - 1) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -170,55 +215,39 @@ __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 
         if (kk > lim) s[kb][r] = -INFINITY;
       }
   }
-  float mx = -INFINITY;
+  bf16x8 pf[4];
+  float ps = exp_tile(s, f.mrun, c_log2, pf);
+  if (__any(!(ps <= kSumLimit))) {
+    float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mt = mx * c_log2;
-  if (__any(mt > f.mrun + kRescaleLog2)) {
-    const float mnew = fmaxf(f.mrun, mt);
-    const float alpha = __builtin_amdgcn_exp2f(f.mrun - (mnew == -INFINITY ? 0.f : mnew));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(f.mrun, mx * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(f.mrun - mnew);
     f.mrun = mnew;
     f.lsum *= alpha;
 #pragma unroll
     for (int dm = 0; dm < C::DM; ++dm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) f.o[dm][r] *= alpha;
+    ps = exp_tile(s, mnew, c_log2, pf);
   }
-  const float mref = f.mrun == -INFINITY ? 0.f : f.mrun;
-  bf16x8 pf[4];
-  float ps = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -mref));
-      s[kb][r] = pv;
-      ps += pv;
-    }
   f.lsum += ps;
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    const int kb = kc >> 1, half = kc & 1;
+  for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      f32x2 two = {s[kb][half * 8 + 2 * e2], s[kb][half * 8 + 2 * e2 + 1]};
-      bf16x2 cv = __builtin_convertvector(two, bf16x2);
-      pf[kc][2 * e2] = cv[0];
-      pf[kc][2 * e2 + 1] = cv[1];
-    }
-  }
+    for (int dm = 0; dm < C::DM; ++dm)
+      f.o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc * C::DM + dm], pf[kc], f.o[dm], 0, 0, 0);
+  read_v(2);
+  read_v(3);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
+  for (int kc = 2; kc < 4; ++kc)
 #pragma unroll
-    for (int dm = 0; dm < C::DM; ++dm) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (dm * 32 + lr) * VROWB +
-                                                        (kc * 16 + lh * 8) * 2);
-      f.o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], f.o[dm], 0, 0, 0);
-    }
-  }
+    for (int dm = 0; dm < C::DM; ++dm)
+      f.o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc * C::DM + dm], pf[kc], f.o[dm], 0, 0, 0);
 }
 
 // Final row sum of this lane's query (both lanes of the pair hold the same value).
