@@ -24,6 +24,13 @@
  * order, or the pages' ZigZag host pairing (h, H-1-h). It changes timing only,
  * never results.
  *
+ * The selection keeps the float64 logits of its first pass for its second pass when
+ * one (block, KV head) pair's logits take at most 512 MiB (G * w * n_b * 8 bytes),
+ * processing pairs in chunks of at most 4 GiB of logits; otherwise, or with the
+ * environment variable SPAVA_SELECT_LOGITS=recompute, it recomputes them. The
+ * workspace size depends on this choice, so the size query and the call must see the
+ * same environment. Scores are bitwise the same either way.
+ *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
  *     allocates no device memory: scratch space is the caller's `workspace`, sized

@@ -12,11 +12,15 @@
 // variant, the rows of a query block that follows the context (every key visible).
 //
 //   rowstats  (m, z) = (max logit, sum exp(logit - max)) of every observer row over
-//             one key split; float64 dot products on v_mfma_f64_16x16x4_f64;
+//             one key split; float64 dot products on v_mfma_f64_16x16x4_f64. When
+//             the plan stores logits, the scaled float64 logits are written too;
 //   merge     combine the key splits of each row into (m, 1/z);
 //   colsum    per key: sum over all observer rows of exp(x - m) / z, in one fixed
 //             order for every key (so equal keys get bitwise-equal scores), then
-//             divide by G*w;
+//             divide by G*w. It reads the stored logits, or recomputes them with the
+//             same products (bitwise the same values either way).
+// With stored logits the pairs are processed in chunks (rowstats, merge, colsum per
+// chunk) so the logit buffer stays bounded.
 //   topl      per (j, g): 8-pass MSB radix select on the float64 bit patterns
 //             (scores are >= 0, so unsigned order is numeric order) to find the
 //             l_j-th largest score, then an in-order compaction that keeps every
@@ -27,7 +31,14 @@
 // holds row 4*r + l/16, column l % 16. Each lane therefore owns a contiguous quarter
 // of the head dimension of one row and one key (slot l/16 <-> d in [l/16*D/4, +D/4)).
 // A wave computes a 32-row x 32-key logit tile per step (2 x 2 MFMA blocks).
+#include <algorithm>
+
 #include "spava_internal.h"
+
+// No floating-point contraction in this file: every product and sum is rounded on its
+// own, so each kernel instantiation (and the stored-logit and recomputing score
+// passes) performs exactly the same operations on the same values.
+#pragma clang fp contract(off)
 
 namespace spava {
 namespace {
@@ -158,25 +169,29 @@ __device__ inline void lse_merge(double& m, double& z, double mo, double zo) {
   m = mn;
 }
 
-// One wave per (jg, 32-row tile, key split). Waves are independent (no barriers).
-template <typename T, int D>
+// One wave per (jg, 32-row tile, key split) for the pairs [jg0, jg0 + npairs). Waves
+// are independent (no barriers). STORE: also write the scaled logits of every visible
+// (row, key) to logits[(jg - jg0)][r][key - s_j].
+template <typename T, int D, bool STORE>
 __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restrict__ q,
                                                        const T* __restrict__ k,
                                                        double2* __restrict__ part,
-                                                       int row_tiles) {
+                                                       double* __restrict__ logits,
+                                                       int row_tiles, int jg0, int npairs) {
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int64_t total = static_cast<int64_t>(p.H - 1) * p.Hkv * row_tiles * p.KS;
+  const int64_t total = static_cast<int64_t>(npairs) * row_tiles * p.KS;
   if (wid >= total) return;
   const int split = static_cast<int>(wid % p.KS);
   const int64_t rest = wid / p.KS;
   const int rt = static_cast<int>(rest % row_tiles);
-  const int jg = static_cast<int>(rest / row_tiles);
+  const int jg = jg0 + static_cast<int>(rest / row_tiles);
   const int j = jg / p.Hkv, g = jg % p.Hkv;
   const int lane = threadIdx.x & 63, col = lane & 15, kg = lane >> 4;
   const int64_t s = static_cast<int64_t>(j) * p.nb;
   const int64_t split_lo = s + static_cast<int64_t>(split) * kScoreSplitKeys;
   const int64_t split_hi = min(s + p.nb, split_lo + kScoreSplitKeys);
   const int r0 = rt * kWaveRows;
+  double* lg = STORE ? logits + static_cast<int64_t>(jg - jg0) * p.R * p.nb : nullptr;
 
   Frag<T, D> qa[2];
   load_rows<T, D>(p, q, j, g, r0, col, kg, qa);
@@ -214,6 +229,8 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
           vis[kb] = key < split_hi && key <= qi[rb][rr];
           x[kb] = p.scale * acc[rb][kb][rr];
           if (vis[kb]) mt = fmax(mt, x[kb]);
+          if (STORE && vis[kb])
+            lg[static_cast<int64_t>(r0 + rb * 16 + 4 * rr + kg) * p.nb + (key - s)] = x[kb];
         }
         if (mt > m[rb][rr]) {
           z[rb][rr] = (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp(m[rb][rr] - mt);
@@ -242,11 +259,13 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
     }
 }
 
+// Rows of the pairs [jg0, jg0 + npairs).
 __global__ void merge_kernel(Plan p, const double2* __restrict__ part,
-                             double2* __restrict__ rowstat) {
-  const int64_t total = static_cast<int64_t>(p.H - 1) * p.Hkv * p.R;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (t >= total) return;
+                             double2* __restrict__ rowstat, int jg0, int npairs) {
+  const int64_t total = static_cast<int64_t>(npairs) * p.R;
+  const int64_t t = static_cast<int64_t>(jg0) * p.R + static_cast<int64_t>(blockIdx.x) * blockDim.x +
+                    threadIdx.x;
+  if (t >= static_cast<int64_t>(jg0) * p.R + total) return;
   const int64_t jg = t / p.R;
   const int r = static_cast<int>(t % p.R);
   double m = -INFINITY, z = 0.0;
@@ -257,7 +276,31 @@ __global__ void merge_kernel(Plan p, const double2* __restrict__ part,
   rowstat[t] = make_double2(m, 1.0 / z);   // (max, 1 / sum)
 }
 
-// One wave per (jg, 32-key tile); loops over all observer rows in a fixed order.
+// exp(x - m) / z of one visible (row, key), else 0 (the same code in both score passes).
+__device__ inline double prob_term(bool vis, double x, double2 mz) {
+  return vis ? exp(x - mz.x) * mz.y : 0.0;
+}
+
+// The four lanes col, col+16, col+32, col+48 hold disjoint row sets of the same key;
+// add them in a fixed order and write the mean.
+__device__ inline void finish_colsum(const Plan& p, const double (&colsum)[2], const int64_t (&key)[2],
+                                     int col, int kg, int jg, int64_t s, int64_t e,
+                                     double* __restrict__ scores) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const double v0 = __shfl(colsum[kb], col);
+    const double v1 = __shfl(colsum[kb], col + 16);
+    const double v2 = __shfl(colsum[kb], col + 32);
+    const double v3 = __shfl(colsum[kb], col + 48);
+    const double sum = ((v0 + v1) + v2) + v3;
+    if (kg == 0 && key[kb] < e)
+      scores[static_cast<int64_t>(jg) * p.nb + (key[kb] - s)] =
+          sum / static_cast<double>(static_cast<int64_t>(p.G) * p.w);
+  }
+}
+
+// One wave per (jg, 32-key tile); loops over all observer rows in a fixed order and
+// recomputes each logit.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void colsum_kernel(Plan p, const T* __restrict__ q,
                                                      const T* __restrict__ k,
@@ -302,23 +345,55 @@ __global__ __launch_bounds__(256) void colsum_kernel(Plan p, const T* __restrict
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const double x = p.scale * acc[rb][kb][rr];
-          colsum[kb] += key[kb] <= qi ? exp(x - mz.x) * mz.y : 0.0;
+          colsum[kb] += prob_term(key[kb] <= qi, x, mz);
         }
       }
   }
-  // The four lanes col, col+16, col+32, col+48 hold disjoint row sets of the same key;
-  // add them in a fixed order.
+  finish_colsum(p, colsum, key, col, kg, jg, s, e, scores);
+}
+
+// Same sums for the pairs [jg0, jg0 + npairs), reading the logits rowstats stored:
+// the rows, their order and every operation match colsum_kernel, so the scores are
+// bitwise the same.
+__global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double* __restrict__ logits,
+                                                            const double2* __restrict__ rowstat,
+                                                            double* __restrict__ scores,
+                                                            int key_tiles, int jg0, int npairs) {
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t total = static_cast<int64_t>(npairs) * key_tiles;
+  if (wid >= total) return;
+  const int kt = static_cast<int>(wid % key_tiles);
+  const int jg = jg0 + static_cast<int>(wid / key_tiles);
+  const int j = jg / p.Hkv;
+  const int lane = threadIdx.x & 63, col = lane & 15, kg = lane >> 4;
+  const int64_t s = static_cast<int64_t>(j) * p.nb;
+  const int64_t e = s + p.nb;
+  const int64_t key0 = s + static_cast<int64_t>(kt) * kWaveKeys;
+  int64_t key[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const double v0 = __shfl(colsum[kb], col);
-    const double v1 = __shfl(colsum[kb], col + 16);
-    const double v2 = __shfl(colsum[kb], col + 32);
-    const double v3 = __shfl(colsum[kb], col + 48);
-    const double sum = ((v0 + v1) + v2) + v3;
-    if (kg == 0 && key[kb] < e)
-      scores[static_cast<int64_t>(jg) * p.nb + (key[kb] - s)] =
-          sum / static_cast<double>(static_cast<int64_t>(p.G) * p.w);
+  for (int kb = 0; kb < 2; ++kb) key[kb] = key0 + kb * 16 + col;
+  const double2* st = rowstat + static_cast<int64_t>(jg) * p.R;
+  const double* lg = logits + static_cast<int64_t>(jg - jg0) * p.R * p.nb;
+
+  double colsum[2] = {0.0, 0.0};
+  for (int r0 = 0; r0 < p.R; r0 += kWaveRows) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = r0 + rb * 16 + 4 * rr + kg;
+        const bool ok = r < p.R;
+        const double2 mz = ok ? st[r] : make_double2(0.0, 0.0);
+        const int64_t qi = ok ? row_key_limit(p, j, r) : -1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bool vis = key[kb] <= qi && key[kb] < e;
+          const double x = vis ? lg[static_cast<int64_t>(r) * p.nb + (key[kb] - s)] : 0.0;
+          colsum[kb] += prob_term(vis, x, mz);
+        }
+      }
   }
+  finish_colsum(p, colsum, key, col, kg, jg, s, e, scores);
 }
 
 // One workgroup per (j, g). 1024 threads = 16 waves of 64.
@@ -428,18 +503,34 @@ static hipError_t launch_select_t(const Plan& p, const T* q, const T* k, int32_t
   double2* part = reinterpret_cast<double2*>(ws + w.rowstat_part);
   double2* rowstat = reinterpret_cast<double2*>(ws + w.rowstat);
   double* scores = scores_out ? scores_out : reinterpret_cast<double*>(ws + w.scores);
-  const int64_t JG = static_cast<int64_t>(p.H - 1) * p.Hkv;
+  double* logits = reinterpret_cast<double*>(ws + w.logits);
+  const int JG = (p.H - 1) * p.Hkv;
   const int row_tiles = static_cast<int>(cdiv(p.R, kWaveRows));
-  const int64_t w1 = JG * row_tiles * p.KS;
-  hipLaunchKernelGGL((rowstats_kernel<T, D>), dim3(static_cast<unsigned>(cdiv(w1, 4))), dim3(256),
-                     0, st, p, q, k, part, row_tiles);
-  const int64_t rows = JG * p.R;
-  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(cdiv(rows, 256))), dim3(256), 0, st,
-                     p, part, rowstat);
   const int key_tiles = static_cast<int>(cdiv(p.nb, kWaveKeys));
-  const int64_t w3 = JG * key_tiles;
-  hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(static_cast<unsigned>(cdiv(w3, 4))), dim3(256), 0,
-                     st, p, q, k, rowstat, scores, key_tiles);
+  if (p.store_logits) {
+    for (int jg0 = 0; jg0 < JG; jg0 += p.pair_chunk) {
+      const int np = std::min(p.pair_chunk, JG - jg0);
+      const int64_t w1 = static_cast<int64_t>(np) * row_tiles * p.KS;
+      hipLaunchKernelGGL((rowstats_kernel<T, D, true>), dim3(static_cast<unsigned>(cdiv(w1, 4))),
+                         dim3(256), 0, st, p, q, k, part, logits, row_tiles, jg0, np);
+      const int64_t rows = static_cast<int64_t>(np) * p.R;
+      hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(cdiv(rows, 256))), dim3(256), 0,
+                         st, p, part, rowstat, jg0, np);
+      const int64_t w3 = static_cast<int64_t>(np) * key_tiles;
+      hipLaunchKernelGGL(colsum_stored_kernel, dim3(static_cast<unsigned>(cdiv(w3, 4))), dim3(256),
+                         0, st, p, logits, rowstat, scores, key_tiles, jg0, np);
+    }
+  } else {
+    const int64_t w1 = static_cast<int64_t>(JG) * row_tiles * p.KS;
+    hipLaunchKernelGGL((rowstats_kernel<T, D, false>), dim3(static_cast<unsigned>(cdiv(w1, 4))),
+                       dim3(256), 0, st, p, q, k, part, nullptr, row_tiles, 0, JG);
+    const int64_t rows = static_cast<int64_t>(JG) * p.R;
+    hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(cdiv(rows, 256))), dim3(256), 0, st,
+                       p, part, rowstat, 0, JG);
+    const int64_t w3 = static_cast<int64_t>(JG) * key_tiles;
+    hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(static_cast<unsigned>(cdiv(w3, 4))), dim3(256),
+                       0, st, p, q, k, rowstat, scores, key_tiles);
+  }
   if (p.l > 0)
     hipLaunchKernelGGL(topl_kernel, dim3(static_cast<unsigned>(JG)), dim3(1024), 0, st, p, scores,
                        idx);

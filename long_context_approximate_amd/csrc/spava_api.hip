@@ -75,12 +75,26 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   // SPAVA_SCHEDULE=lpt|natural|zigzag picks the attention dispatch order (default:
   // longest first). Every order computes the same values; only timing differs.
   p->obs_query = 0;
+  set_logit_store(p);
   p->sched = kSchedLongestFirst;
   if (const char* e = getenv("SPAVA_SCHEDULE")) {
     if (strcmp(e, "natural") == 0) p->sched = kSchedNatural;
     else if (strcmp(e, "zigzag") == 0) p->sched = kSchedZigZag;
   }
   return SPAVA_OK;
+}
+
+// SPAVA_SELECT_LOGITS=recompute makes the score pass recompute the logits instead of
+// storing them (less workspace, more time). Scores are bitwise the same either way.
+void set_logit_store(Plan* p) {
+  const int64_t jg = static_cast<int64_t>(p->H > 1 ? p->H - 1 : 0) * p->Hkv;
+  const int64_t per_pair = static_cast<int64_t>(p->R) * p->nb * static_cast<int64_t>(sizeof(double));
+  const char* e = getenv("SPAVA_SELECT_LOGITS");
+  const bool recompute = e && strcmp(e, "recompute") == 0;
+  p->store_logits = (!recompute && jg > 0 && per_pair <= kLogitPairBytes) ? 1 : 0;
+  p->pair_chunk = p->store_logits
+                      ? static_cast<int>(std::max<int64_t>(1, std::min(jg, kLogitChunkBytes / per_pair)))
+                      : 0;
 }
 
 SelectWs select_ws_layout(const Plan& p) {
@@ -90,6 +104,9 @@ SelectWs select_ws_layout(const Plan& p) {
   w.rowstat_part = region(cur, jg * p.KS * p.R * 2 * sizeof(double));
   w.rowstat = region(cur, jg * p.R * 2 * sizeof(double));
   w.scores = region(cur, jg * p.nb * sizeof(double));
+  w.logits = region(cur, p.store_logits ? static_cast<size_t>(p.pair_chunk) * p.R * p.nb *
+                                              sizeof(double)
+                                        : 0);
   w.total = cur;
   return w;
 }
@@ -247,6 +264,7 @@ static spava_status make_query_select_plan(const spava_shape* shape, int64_t n_q
   p->w = static_cast<int>(n_query);
   p->R = static_cast<int>(n_query * p->G);
   p->obs_query = 1;
+  set_logit_store(p);
   return SPAVA_OK;
 }
 

@@ -9,9 +9,14 @@
 namespace spava {
 
 constexpr int kKeyTile = 64;     // keys per LDS tile in the attention kernels
-constexpr int kQTile = 256;      // queries per attention workgroup (4 waves x 64)
+constexpr int kQTile = 256;      // queries per attention workgroup (8 waves x 32)
 constexpr int kScoreTile = 64;   // rows and keys per fp64 score workgroup tile
 constexpr int kScoreSplitKeys = 2048;  // keys per split in the row-statistics pass
+// The score pass keeps the float64 logits of the row-statistics pass when one
+// (block, KV head) pair's logits fit in kLogitPairBytes; pairs are then processed in
+// chunks of at most kLogitChunkBytes of logits. Otherwise the logits are recomputed.
+constexpr int64_t kLogitPairBytes = int64_t(512) << 20;
+constexpr int64_t kLogitChunkBytes = int64_t(4) << 30;
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -34,7 +39,12 @@ struct Plan {
   int sched;        // query-tile dispatch order (ScheduleMode); never changes results
   int obs_query;    // selection observers: 0 = last w queries of each block,
                     // 1 = the w rows of a query block (every key visible)
+  int store_logits; // 1: the score pass reads stored logits instead of recomputing
+  int pair_chunk;   // (block, KV head) pairs per chunk when logits are stored
 };
+
+// Decide whether the selection stores its logits (after R is final).
+void set_logit_store(Plan* p);
 
 // Dispatch order of the (block, query tile) pairs of the attention grid.
 enum ScheduleMode { kSchedLongestFirst = 0, kSchedNatural = 1, kSchedZigZag = 2 };
@@ -46,7 +56,7 @@ __host__ __device__ inline int prefix_len(const Plan& p, int h) {
 
 // Workspace carving (byte offsets, 256-byte aligned regions).
 struct SelectWs {
-  size_t rowstat_part, rowstat, scores, total;
+  size_t rowstat_part, rowstat, scores, logits, total;
 };
 struct AttnWs {
   size_t kpre, vpre, vtloc, order, total;

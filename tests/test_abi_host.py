@@ -78,6 +78,15 @@ def test_null_shape(lib):
     assert lib.spava_attn_workspace_bytes(ctypes.byref(_shape()), None) == ERR_NULL
 
 
+def _logit_bytes(jg, R, nb):
+    """Stored float64 logits: one chunk of (block, KV head) pairs when a pair fits in
+    512 MiB, at most 4 GiB per chunk; none otherwise."""
+    per_pair = R * nb * 8
+    if jg == 0 or per_pair > (512 << 20):
+        return 0
+    return max(1, min(jg, (4 << 30) // per_pair)) * per_pair
+
+
 def _expected_ws(sh):
     def r(b):
         return (b + 255) // 256 * 256
@@ -87,7 +96,7 @@ def _expected_ws(sh):
     es = 2 if sh.dtype == spava.SPAVA_BF16 else 4
     ks = -(-nb // 2048)
     jg = (H - 1) * hkv
-    sel = r(jg * ks * G * w * 16) + r(jg * G * w * 16) + r(jg * nb * 8)
+    sel = r(jg * ks * G * w * 16) + r(jg * G * w * 16) + r(jg * nb * 8) + r(_logit_bytes(jg, G * w, nb))
     l0 = min(sh.passing_len, nb - sh.anchor_len) if H > 1 else 0
     l1 = min(sh.passing_len, nb) if H > 2 else 0
     lmax = sh.anchor_len + l0 + (H - 2) * l1 if H > 1 else 0
@@ -99,12 +108,29 @@ def _expected_ws(sh):
 
 
 @pytest.mark.parametrize("kw", [{}, {"num_hosts": 8, "seq_len": 8192}, {"dtype": 1, "head_dim": 64},
-                                {"num_hosts": 2}, {"seq_len": 3000, "num_hosts": 3, "anchor_len": 100}])
+                                {"num_hosts": 2}, {"seq_len": 3000, "num_hosts": 3, "anchor_len": 100},
+                                # 512 MiB of logits per pair: chunks of 8 pairs
+                                {"seq_len": 16 * 16384, "num_hosts": 16, "num_q_heads": 32,
+                                 "num_kv_heads": 8, "window": 1024, "anchor_len": 4096,
+                                 "passing_len": 2048},
+                                # far above 512 MiB per pair: logits recomputed
+                                {"seq_len": 262144, "num_hosts": 2, "num_q_heads": 8,
+                                 "num_kv_heads": 1, "window": 65536, "anchor_len": 1024}])
 def test_workspace_sizes(lib, kw):
     sh = _shape(**kw)
     sel, attn = _expected_ws(sh)
     assert spava.spava_select_workspace_bytes(sh) == sel
     assert spava.spava_attn_workspace_bytes(sh) == attn
+
+
+def test_recompute_switch_drops_the_logit_workspace(lib, monkeypatch):
+    sh = _shape()
+    with_logits = spava.spava_select_workspace_bytes(sh)
+    monkeypatch.setenv("SPAVA_SELECT_LOGITS", "recompute")
+    without = spava.spava_select_workspace_bytes(sh)
+    def r(b):
+        return (b + 255) // 256 * 256
+    assert with_logits - without == r(_logit_bytes(3 * 2, 4 * 32, 1024))
 
 
 def test_calls_reject_bad_arguments_without_touching_the_gpu(lib):
@@ -159,7 +185,8 @@ def test_query_selection_entry_validation(lib):
     def r(b):
         return (b + 255) // 256 * 256
     jg, R = 3 * 2, 4 * 100
-    assert n.value == r(jg * 1 * R * 16) + r(jg * R * 16) + r(jg * 1024 * 8)
+    assert n.value == (r(jg * 1 * R * 16) + r(jg * R * 16) + r(jg * 1024 * 8)
+                       + r(_logit_bytes(jg, R, 1024)))
     f = lib.spava_select_passing_query
     s = ctypes.byref(sh)
     assert f(s, 100, None, FAKE, FAKE, None, FAKE, n.value, None) == ERR_NULL

@@ -224,6 +224,25 @@ def test_schedules_give_identical_results(monkeypatch):
             assert np.array_equal(results[mode][key], results["lpt"][key]), (mode, key)
 
 
+@pytest.mark.parametrize("name", ["small", "h4_16k"])
+def test_stored_and_recomputed_logits_agree_bitwise(monkeypatch, name):
+    # The score pass either reads the logits its first pass stored or recomputes them
+    # with the same products; both must give bitwise-equal scores and indices, and
+    # match the oracle.
+    cfg = small_config() if name == "small" else CONFIGS[name]
+    x = make_inputs(cfg)
+    results = {}
+    for mode in ("store", "recompute"):
+        monkeypatch.setenv("SPAVA_SELECT_LOGITS", mode)
+        results[mode], _ = _gpu_run(cfg, x)
+    for key in ("idx", "scores"):
+        assert np.array_equal(results["store"][key], results["recompute"][key]), key
+    sh = oracle.shape_of(cfg)
+    scores = oracle.all_window_scores(sh, x["q"], x["k"])
+    _check_selection(cfg, results["store"], {"idx": oracle.select_passing(sh, scores),
+                                             "scores": scores})
+
+
 # ------------------------------------------------------------- query block B_qr
 
 def _query_case(cfg, x, nq_take=None, context=None):
@@ -321,6 +340,18 @@ def test_query_aware_selection_parity(cfg, nq):
     ref_sc = oracle.all_query_scores(sh, q_qr, x["k"])
     ref_idx = oracle.select_passing(sh, ref_sc)
     _check_selection(cfg, {"idx": idx, "scores": sc}, {"idx": ref_idx, "scores": ref_sc})
+
+
+def test_query_aware_selection_recompute_path(monkeypatch):
+    cfg, nq = QSEL[2]
+    x = make_inputs(cfg)
+    qcfg = cfg.with_(seq_len=nq, num_hosts=1, anchor_len=0, window=1, seed=cfg.seed + 500)
+    q_qr = make_inputs(qcfg)["q"]
+    stored = _gpu_query_select(cfg, x, q_qr)
+    monkeypatch.setenv("SPAVA_SELECT_LOGITS", "recompute")
+    recomputed = _gpu_query_select(cfg, x, q_qr)
+    assert np.array_equal(stored[0], recomputed[0])
+    assert np.array_equal(stored[1], recomputed[1])
 
 
 def test_query_aware_ties_go_to_lower_positions():
