@@ -18,6 +18,8 @@
  * A third call attends a query block (the text question after the context) to the
  * whole context exactly, by per-host partials merged with their log-sum-exp:
  *   spava_query_attn_fwd.
+ * spava_layer_overlap_fwd does the two calls of a layer at once, overlapping the
+ * selection with the part of the attention that needs no passing rows.
  *
  * The environment variable SPAVA_SCHEDULE (lpt | natural | zigzag) selects the
  * dispatch order of the attention's query tiles: longest first (default), block
@@ -221,6 +223,44 @@ spava_status spava_query_attn_fwd(const spava_shape* shape, int64_t n_query, con
                                   const void* k_qr, const void* v_qr, const void* k,
                                   const void* v, void* out_qr, float* lse_qr, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace spava_layer_overlap_fwd needs (host only). */
+spava_status spava_layer_overlap_workspace_bytes(const spava_shape* shape, size_t* bytes);
+
+/*
+ * One prefill layer with the selection overlapped ("Systemseitige Optimierungen" of
+ * the explainer "APB-V: ...": passing blocks are transferred while attention computes;
+ * on one GPU the transfer is the selection and gather, and the independent work is
+ * the anchor and the local context).
+ *
+ * Computes exactly what spava_select_passing followed by spava_approx_attn_fwd compute,
+ * with the attention split in two parts merged by log-sum-exp:
+ *   on side_stream  the selection (passing_idx, scores_out), then the gather of the
+ *                   passing rows;
+ *   on stream       part X, every query against the whole 64-key tiles of the anchor
+ *                   and its local keys (block 0 is complete after it), concurrently;
+ *                   then, after the side stream, part Y: the rest of the prefix (the
+ *                   passing rows, and the anchor's ragged last tile when A % 64 != 0),
+ *                   merged with part X's (O, LSE) into out and lse_out.
+ * Outputs match the two-call path to rounding (the merge changes the summation order;
+ * indices and scores are the same).
+ *
+ *   q, k, v, passing_idx, scores_out, out, lse_out   as in the two calls above
+ *   workspace     device, >= spava_layer_overlap_workspace_bytes bytes (the selection's
+ *                 and the attention's workspaces plus part X's float32 (O, LSE),
+ *                 N*Hq*d*4 + Hq*N*4 bytes)
+ *   stream        hipStream_t the call is ordered on; every result is ready once it
+ *                 reaches this point
+ *   side_stream   a second hipStream_t (NULL = the default stream). It first waits for
+ *                 work already enqueued on `stream`, so inputs produced there are safe.
+ *                 Using the same stream twice is correct but overlaps nothing.
+ * bf16 only (SPAVA_ERR_DTYPE for f32). With H == 1 or l == 0 nothing needs selecting
+ * and the plain attention runs on `stream`.
+ */
+spava_status spava_layer_overlap_fwd(const spava_shape* shape, const void* q, const void* k,
+                                     const void* v, int32_t* passing_idx, double* scores_out,
+                                     void* out, float* lse_out, void* workspace,
+                                     size_t workspace_bytes, void* stream, void* side_stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,13 @@
 //              each tile is one flash step (attn_common.h): S^T = K Q^T and
 //              O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with float32 accumulators
 //              and an online softmax in float32 with exp2 and a folded scale.
+//
+// Split mode (the one-GPU form of the pages' overlap of passing-block transfers with
+// compute, "Systemseitige Optimierungen"): part X attends every query to the whole
+// anchor tiles and its local keys, which need no selection, and stores (O, LSE) per
+// query; part Y attends to the rest of the prefix (the passing rows, with the
+// anchor's ragged last tile) and merges with part X by log-sum-exp. X can run while
+// the selection runs on another stream.
 #include "attn_common.h"
 
 namespace spava {
@@ -43,25 +50,29 @@ __device__ inline int64_t prefix_source(const Plan& p, const int32_t* idx, int g
   return (src >= lo && src < s + p.nb) ? src : -1;
 }
 
-// grid.x: [0, Lpad/64) prefix tiles, then H*loc_tiles local V tiles; grid.y: KV head.
+// Whole anchor tiles: prefix tiles [0, A / 64) hold anchor rows only.
+__host__ __device__ inline int anchor_tiles(const Plan& p) { return p.A / BN; }
+
+// grid.x: prefix tiles [t0, t1), then (with_local) H*loc_tiles local V tiles;
+// grid.y: KV head.
 template <int D>
 __global__ __launch_bounds__(256) void prep_kernel(Plan p, const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v,
                                                    const int32_t* __restrict__ idx,
                                                    uint16_t* __restrict__ kpre,
                                                    uint16_t* __restrict__ vtpre,
-                                                   uint16_t* __restrict__ vtloc) {
+                                                   uint16_t* __restrict__ vtloc, int t0, int t1) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[BN][D + 8];
   __shared__ int64_t src_tok[BN];
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int npre_tiles = p.Lpad / BN;
-  const bool is_prefix = static_cast<int>(blockIdx.x) < npre_tiles;
+  const bool is_prefix = static_cast<int>(blockIdx.x) < t1 - t0;
   int tile, h = 0;
   if (is_prefix) {
-    tile = blockIdx.x;
+    tile = t0 + blockIdx.x;
   } else {
-    const int lt = blockIdx.x - npre_tiles;
+    const int lt = blockIdx.x - (t1 - t0);
     h = lt / p.loc_tiles;
     tile = lt % p.loc_tiles;
   }
@@ -98,16 +109,30 @@ __global__ __launch_bounds__(256) void prep_kernel(Plan p, const uint16_t* __res
   store_vt_tile<D>(Vs, dst);
 }
 
-__device__ inline int pair_cost(const Plan& p, int pair) {
+// Prefix tiles [pt0, pt1) and whether local tiles follow, for block h in a mode.
+struct TileRange {
+  int pt0, pt1, local;
+};
+__device__ inline TileRange tile_range(const Plan& p, int h, int mode) {
+  const int npre = (prefix_len(p, h) + BN - 1) / BN;
+  const int nax = h >= 1 ? anchor_tiles(p) : 0;
+  if (mode == kAttnPartX) return {0, nax, 1};
+  if (mode == kAttnPartY) return {nax, npre, 0};
+  return {0, npre, 1};
+}
+
+__device__ inline int pair_cost(const Plan& p, int pair, int mode) {
   const int h = pair / p.T, t = pair % p.T;
   const int loc = min(p.nb, (t + 1) * kQTile);
-  return (prefix_len(p, h) + BN - 1) / BN + (loc + BN - 1) / BN;
+  const TileRange tr = tile_range(p, h, mode);
+  return (tr.pt1 - tr.pt0) + (tr.local ? (loc + BN - 1) / BN : 0);
 }
 
 // order[rank] = pair (pair = block * T + query tile). Longest first: pairs ranked by
 // decreasing key-tile count, ties by pair index. Natural: block-major. ZigZag: blocks
 // paired as (p, H-1-p), the pages' host pairing, tiles of a pair alternating.
-__global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restrict__ order) {
+__global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restrict__ order,
+                                                       int mode) {
   const int P = p.H * p.T;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= P) return;
@@ -120,9 +145,9 @@ __global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restri
     const int pr = min(h, mirror);
     rank = (h == mirror) ? pr * 2 * p.T + t : pr * 2 * p.T + 2 * t + (h > mirror ? 1 : 0);
   } else {
-    const int ci = pair_cost(p, i);
+    const int ci = pair_cost(p, i, mode);
     for (int j = 0; j < P; ++j) {
-      const int cj = pair_cost(p, j);
+      const int cj = pair_cost(p, j, mode);
       rank += (cj > ci) || (cj == ci && j < i);
     }
   }
@@ -134,7 +159,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     Plan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kpre, const uint16_t* __restrict__ vtpre,
     const uint16_t* __restrict__ vtloc, const int32_t* __restrict__ order,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int NG, float c_log2) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int NG, float c_log2, int mode,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
 
@@ -153,10 +179,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   const int64_t e_h = s_h + p.nb;
   const int64_t q0 = s_h + static_cast<int64_t>(t) * kQTile;
   const int64_t q_end = min(q0 + kQTile, e_h);
+  // Part Y of block 0 has nothing to do: part X wrote its final output.
+  if (mode == kAttnPartY && h == 0) return;
   const int L = prefix_len(p, h);
   const int npre = (L + BN - 1) / BN;
-  const int nloc = static_cast<int>((q_end - s_h + BN - 1) / BN);
-  const int ntiles = npre + nloc;
+  const TileRange tr = tile_range(p, h, mode);
+  const int np = tr.pt1 - tr.pt0;
+  const int nloc = tr.local ? static_cast<int>((q_end - s_h + BN - 1) / BN) : 0;
+  const int ntiles = np + nloc;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -174,13 +204,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   // place and V^T from the block's transposed tiles.
   TileStage<D> stage;
   auto load_tile = [&](int it) {
-    const bool pre = it < npre;
-    const int lt = it - npre;
+    const bool pre = it < np;
+    const int pt = tr.pt0 + it;
+    const int lt = it - np;
     const int64_t key0 = s_h + static_cast<int64_t>(lt) * BN;
-    const uint16_t* kb = pre ? kpre_g + static_cast<int64_t>(it) * BN * D : k_g + key0 * p.kvs_tok;
+    const uint16_t* kb = pre ? kpre_g + static_cast<int64_t>(pt) * BN * D : k_g + key0 * p.kvs_tok;
     const int64_t krow = pre ? D : p.kvs_tok;
     const int64_t kvalid = pre ? BN : e_h - key0;
-    const uint16_t* vb = pre ? vtpre_g + static_cast<int64_t>(it) * D * BN
+    const uint16_t* vb = pre ? vtpre_g + static_cast<int64_t>(pt) * D * BN
                              : vtloc_gh + static_cast<int64_t>(lt) * D * BN;
     stage.load(kb, krow, kvalid, vb);
   };
@@ -190,20 +221,23 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   Flash<D> f;
   f.init();
 
-  load_tile(0);
-  stage.store(smem);
+  if (ntiles > 0) {
+    load_tile(0);
+    stage.store(smem);
+  }
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) load_tile(it + 1);
-    const bool local = it >= npre;
-    const int64_t key0 = local ? s_h + static_cast<int64_t>(it - npre) * BN : 0;
+    const bool local = it >= np;
+    const int pt = tr.pt0 + it;
+    const int64_t key0 = local ? s_h + static_cast<int64_t>(it - np) * BN : 0;
     // Last visible key of the tile: the prefix length in the last prefix tile, the
     // causal diagonal in a local tile. Tiles past this wave's queries are processed
     // fully masked (lim = -1) rather than branched around, which keeps the O
     // accumulators in place across iterations.
     int lim = BN - 1;
-    if (!local && it == npre - 1 && (L % BN) != 0) lim = L - it * BN - 1;
+    if (!local && pt == npre - 1 && (L % BN) != 0) lim = L - pt * BN - 1;
     if (local && key0 + BN - 1 > qw0) {
       const int64_t rel = qi - key0;               // integer select (no floating max)
       lim = rel < 0 ? -1 : static_cast<int>(rel);
@@ -217,15 +251,47 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
 
   // ---- epilogue: normalise, round to bf16, write O and LSE
   const float ltot = flash_rowsum<D>(f);
-  if (qi < e_h) {
+  if (qi < e_h && mode == kAttnPartX && h >= 1) {
+    // Part X of a block with a prefix: keep the normalised partial (O, log2-LSE).
     const float inv = 1.f / ltot;
+    float* po = part_o + (qi * p.Hq + hq) * D;
+#pragma unroll
+    for (int dm = 0; dm < C::DM; ++dm)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        float4 v4;
+        v4.x = f.o[dm][grp * 4 + 0] * inv;
+        v4.y = f.o[dm][grp * 4 + 1] * inv;
+        v4.z = f.o[dm][grp * 4 + 2] * inv;
+        v4.w = f.o[dm][grp * 4 + 3] * inv;
+        *reinterpret_cast<float4*>(po + out_dim<D>(dm, grp, lh)) = v4;
+      }
+    if (lh == 0) part_lse[static_cast<int64_t>(hq) * p.N + qi] = f.mrun + log2f(ltot);
+  } else if (qi < e_h) {
+    // Full output, or part Y merged with part X: O = (wx O_x + wy O_y) / (wx + wy) with
+    // w = 2^LSE relative to the larger of the two LSEs.
+    float cx = 0.f, cy = 1.f / ltot, lse2 = f.mrun + log2f(ltot);
+    const float* po = nullptr;
+    if (mode == kAttnPartY) {
+      const float lx = part_lse[static_cast<int64_t>(hq) * p.N + qi];
+      const float ly = ltot > 0.f ? f.mrun + log2f(ltot) : -INFINITY;
+      const float mx = fmaxf(lx, ly);
+      const float wx = exp2f(lx - mx), wy = ltot > 0.f ? exp2f(ly - mx) : 0.f;
+      const float den = wx + wy;
+      cx = wx / den;
+      cy = ltot > 0.f ? wy / (ltot * den) : 0.f;
+      lse2 = mx + log2f(den);
+      po = part_o + (qi * p.Hq + hq) * D;
+    }
     uint16_t* op = out + qi * p.os_tok + hq * p.os_head;
 #pragma unroll
     for (int dm = 0; dm < C::DM; ++dm)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        f32x2 lo = {f.o[dm][grp * 4 + 0] * inv, f.o[dm][grp * 4 + 1] * inv};
-        f32x2 hi = {f.o[dm][grp * 4 + 2] * inv, f.o[dm][grp * 4 + 3] * inv};
+        float4 ox = {0.f, 0.f, 0.f, 0.f};
+        if (po) ox = *reinterpret_cast<const float4*>(po + out_dim<D>(dm, grp, lh));
+        f32x2 lo = {ox.x * cx + f.o[dm][grp * 4 + 0] * cy, ox.y * cx + f.o[dm][grp * 4 + 1] * cy};
+        f32x2 hi = {ox.z * cx + f.o[dm][grp * 4 + 2] * cy, ox.w * cx + f.o[dm][grp * 4 + 3] * cy};
         bf16x2 blo = __builtin_convertvector(lo, bf16x2);
         bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
         uint2 pk;
@@ -233,29 +299,53 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
         pk.y = __builtin_bit_cast(uint32_t, bhi);
         *reinterpret_cast<uint2*>(op + out_dim<D>(dm, grp, lh)) = pk;
       }
-    if (lse && lh == 0)
-      lse[static_cast<int64_t>(hq) * p.N + qi] = (f.mrun + log2f(ltot)) * 0.69314718055994531f;
+    if (lse && lh == 0) lse[static_cast<int64_t>(hq) * p.N + qi] = lse2 * 0.69314718055994531f;
   }
+}
+
+struct AttnPtrs {
+  uint16_t *kpre, *vtpre, *vtloc;
+  int32_t *order, *order2;
+};
+static AttnPtrs attn_ptrs(const Plan& p, char* ws) {
+  const AttnWs w = attn_ws_layout(p);
+  return {reinterpret_cast<uint16_t*>(ws + w.kpre), reinterpret_cast<uint16_t*>(ws + w.vpre),
+          reinterpret_cast<uint16_t*>(ws + w.vtloc), reinterpret_cast<int32_t*>(ws + w.order),
+          reinterpret_cast<int32_t*>(ws + w.order2)};
+}
+
+// Gather prefix tiles [t0, t1) (and, with_local, every block's local V^T tiles).
+template <int D>
+void launch_prep(const Plan& p, const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                 const AttnPtrs& a, int t0, int t1, bool with_local, hipStream_t st) {
+  const unsigned gx = static_cast<unsigned>((t1 - t0) + (with_local ? p.H * p.loc_tiles : 0));
+  if (gx == 0) return;
+  hipLaunchKernelGGL(prep_kernel<D>, dim3(gx, p.Hkv), dim3(256), 0, st, p, k, v, idx, a.kpre,
+                     a.vtpre, a.vtloc, t0, t1);
+}
+
+// Order the (block, query tile) pairs for `mode` and run the attention kernel.
+template <int D>
+void launch_attn_mode(const Plan& p, const uint16_t* q, const uint16_t* k, const AttnPtrs& a,
+                      int32_t* order, uint16_t* out, float* lse, int mode, float* part_o,
+                      float* part_lse, hipStream_t st) {
+  const int P = p.H * p.T;
+  hipLaunchKernelGGL(schedule_kernel, dim3(static_cast<unsigned>(cdiv(P, 256))), dim3(256), 0, st,
+                     p, order, mode);
+  const int NG = P * p.Hkv;
+  const int64_t grid = round_up(NG, 8) * p.G;
+  const float c_log2 = static_cast<float>(p.scale * 1.4426950408889634);
+  hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p, q,
+                     k, a.kpre, a.vtpre, a.vtloc, order, out, lse, NG, c_log2, mode, part_o,
+                     part_lse);
 }
 
 template <int D>
 hipError_t launch_d(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* idx, uint16_t* out, float* lse, char* ws, hipStream_t st) {
-  const AttnWs w = attn_ws_layout(p);
-  uint16_t* kpre = reinterpret_cast<uint16_t*>(ws + w.kpre);
-  uint16_t* vtpre = reinterpret_cast<uint16_t*>(ws + w.vpre);
-  uint16_t* vtloc = reinterpret_cast<uint16_t*>(ws + w.vtloc);
-  int32_t* order = reinterpret_cast<int32_t*>(ws + w.order);
-  const unsigned prep_x = static_cast<unsigned>(p.Lpad / BN + p.H * p.loc_tiles);
-  hipLaunchKernelGGL(prep_kernel<D>, dim3(prep_x, p.Hkv), dim3(256), 0, st, p, k, v, idx, kpre,
-                     vtpre, vtloc);
-  const int P = p.H * p.T;
-  hipLaunchKernelGGL(schedule_kernel, dim3(static_cast<unsigned>(cdiv(P, 256))), dim3(256), 0, st,
-                     p, order);
-  const int NG = P * p.Hkv;
-  const int64_t grid = round_up(NG, 8) * p.G;
-  const float c_log2 = static_cast<float>(p.scale * 1.4426950408889634);
-  hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p, q, k, kpre, vtpre, vtloc, order, out, lse, NG, c_log2);
+  const AttnPtrs a = attn_ptrs(p, ws);
+  launch_prep<D>(p, k, v, idx, a, 0, p.Lpad / BN, true, st);
+  launch_attn_mode<D>(p, q, k, a, a.order, out, lse, kAttnFull, nullptr, nullptr, st);
   return hipGetLastError();
 }
 
@@ -269,6 +359,48 @@ hipError_t launch_attn_bf16(const Plan& p, const void* q, const void* k, const v
   auto oo = static_cast<uint16_t*>(out);
   if (p.D == 128) return launch_d<128>(p, qq, kk, vv, idx, oo, lse, ws, st);
   return launch_d<64>(p, qq, kk, vv, idx, oo, lse, ws, st);
+}
+
+hipError_t launch_attn_bf16_part_x(const Plan& p, const void* q, const void* k, const void* v,
+                                   void* out, float* lse, char* ws, float* part_o,
+                                   float* part_lse, hipStream_t st) {
+  auto qq = static_cast<const uint16_t*>(q);
+  auto kk = static_cast<const uint16_t*>(k);
+  auto vv = static_cast<const uint16_t*>(v);
+  auto oo = static_cast<uint16_t*>(out);
+  const AttnPtrs a = attn_ptrs(p, ws);
+  if (p.D == 128) {
+    launch_prep<128>(p, kk, vv, nullptr, a, 0, anchor_tiles(p), true, st);
+    launch_attn_mode<128>(p, qq, kk, a, a.order, oo, lse, kAttnPartX, part_o, part_lse, st);
+  } else {
+    launch_prep<64>(p, kk, vv, nullptr, a, 0, anchor_tiles(p), true, st);
+    launch_attn_mode<64>(p, qq, kk, a, a.order, oo, lse, kAttnPartX, part_o, part_lse, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_gather_passing(const Plan& p, const void* k, const void* v,
+                                           const int32_t* idx, char* ws, hipStream_t st) {
+  auto kk = static_cast<const uint16_t*>(k);
+  auto vv = static_cast<const uint16_t*>(v);
+  const AttnPtrs a = attn_ptrs(p, ws);
+  if (p.D == 128) launch_prep<128>(p, kk, vv, idx, a, anchor_tiles(p), p.Lpad / BN, false, st);
+  else launch_prep<64>(p, kk, vv, idx, a, anchor_tiles(p), p.Lpad / BN, false, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_part_y(const Plan& p, const void* q, const void* k, void* out,
+                                   float* lse, char* ws, float* part_o, float* part_lse,
+                                   hipStream_t st) {
+  auto qq = static_cast<const uint16_t*>(q);
+  auto kk = static_cast<const uint16_t*>(k);
+  auto oo = static_cast<uint16_t*>(out);
+  const AttnPtrs a = attn_ptrs(p, ws);
+  if (p.D == 128)
+    launch_attn_mode<128>(p, qq, kk, a, a.order2, oo, lse, kAttnPartY, part_o, part_lse, st);
+  else
+    launch_attn_mode<64>(p, qq, kk, a, a.order2, oo, lse, kAttnPartY, part_o, part_lse, st);
+  return hipGetLastError();
 }
 
 }  // namespace spava

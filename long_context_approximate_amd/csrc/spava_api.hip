@@ -122,6 +122,18 @@ AttnWs attn_ws_layout(const Plan& p) {
                          : 0;
   w.vtloc = region(cur, loc);
   w.order = region(cur, static_cast<size_t>(p.H) * p.T * sizeof(int32_t));
+  w.order2 = region(cur, static_cast<size_t>(p.H) * p.T * sizeof(int32_t));
+  w.total = cur;
+  return w;
+}
+
+OverlapWs overlap_ws_layout(const Plan& p) {
+  OverlapWs w{};
+  size_t cur = 0;
+  w.select = region(cur, select_ws_layout(p).total);
+  w.attn = region(cur, attn_ws_layout(p).total);
+  w.part_o = region(cur, static_cast<size_t>(p.N) * p.Hq * p.D * sizeof(float));
+  w.part_lse = region(cur, static_cast<size_t>(p.Hq) * p.N * sizeof(float));
   w.total = cur;
   return w;
 }
@@ -335,6 +347,78 @@ spava_status spava_query_attn_fwd(const spava_shape* shape, int64_t n_query, con
   hipError_t e = launch_query(p, n_query, q_qr, k_qr, v_qr, k, v, out_qr, lse_qr,
                               static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
+}
+
+spava_status spava_layer_overlap_workspace_bytes(const spava_shape* shape, size_t* bytes) {
+  if (!bytes) return SPAVA_ERR_NULL;
+  Plan p;
+  spava_status st = make_plan(shape, &p);
+  if (st != SPAVA_OK) return st;
+  *bytes = overlap_ws_layout(p).total;
+  return SPAVA_OK;
+}
+
+spava_status spava_layer_overlap_fwd(const spava_shape* shape, const void* q, const void* k,
+                                     const void* v, int32_t* passing_idx, double* scores_out,
+                                     void* out, float* lse_out, void* workspace,
+                                     size_t workspace_bytes, void* stream, void* side_stream) {
+  Plan p;
+  spava_status st = make_plan(shape, &p);
+  if (st != SPAVA_OK) return st;
+  if (p.dtype != SPAVA_BF16) return SPAVA_ERR_DTYPE;
+  if (!q || !k || !v || !out || !workspace) return SPAVA_ERR_NULL;
+  const bool any = p.H > 1 && p.l > 0;
+  if (any && !passing_idx) return SPAVA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return SPAVA_ERR_ALIGN;
+  if (passing_idx && (reinterpret_cast<uintptr_t>(passing_idx) & 3u)) return SPAVA_ERR_ALIGN;
+  if (scores_out && (reinterpret_cast<uintptr_t>(scores_out) & 7u)) return SPAVA_ERR_ALIGN;
+  if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)) return SPAVA_ERR_ALIGN;
+  const OverlapWs w = overlap_ws_layout(p);
+  if (workspace_bytes < w.total) return SPAVA_ERR_WORKSPACE;
+  st = check_device();
+  if (st != SPAVA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t main_st = static_cast<hipStream_t>(stream);
+  hipStream_t side_st = static_cast<hipStream_t>(side_stream);
+  // Nothing to select: the plain layer on the main stream.
+  if (!any) {
+    if (p.H > 1 && scores_out &&
+        launch_select(p, q, k, passing_idx, scores_out, ws + w.select, main_st) != hipSuccess)
+      return SPAVA_ERR_HIP;
+    return launch_attn_bf16(p, q, k, v, passing_idx, out, lse_out, ws + w.attn, main_st) ==
+                   hipSuccess
+               ? SPAVA_OK
+               : SPAVA_ERR_HIP;
+  }
+  float* part_o = reinterpret_cast<float*>(ws + w.part_o);
+  float* part_lse = reinterpret_cast<float*>(ws + w.part_lse);
+  hipEvent_t inputs_ready = nullptr, passing_ready = nullptr;
+  if (hipEventCreateWithFlags(&inputs_ready, hipEventDisableTiming) != hipSuccess)
+    return SPAVA_ERR_HIP;
+  if (hipEventCreateWithFlags(&passing_ready, hipEventDisableTiming) != hipSuccess) {
+    (void)hipEventDestroy(inputs_ready);
+    return SPAVA_ERR_HIP;
+  }
+  bool ok = true;
+  // Side stream: selection, then the gather of the passing rows. It starts once the
+  // main stream has reached this call (the inputs are ready there).
+  ok = ok && hipEventRecord(inputs_ready, main_st) == hipSuccess;
+  ok = ok && hipStreamWaitEvent(side_st, inputs_ready, 0) == hipSuccess;
+  ok = ok && launch_select(p, q, k, passing_idx, scores_out, ws + w.select, side_st) == hipSuccess;
+  ok = ok && launch_attn_bf16_gather_passing(p, k, v, passing_idx, ws + w.attn, side_st) ==
+                 hipSuccess;
+  ok = ok && hipEventRecord(passing_ready, side_st) == hipSuccess;
+  // Main stream: part X meanwhile, then part Y once the passing rows are gathered.
+  ok = ok && launch_attn_bf16_part_x(p, q, k, v, out, lse_out, ws + w.attn, part_o, part_lse,
+                                     main_st) == hipSuccess;
+  ok = ok && hipStreamWaitEvent(main_st, passing_ready, 0) == hipSuccess;
+  ok = ok && launch_attn_bf16_part_y(p, q, k, out, lse_out, ws + w.attn, part_o, part_lse,
+                                     main_st) == hipSuccess;
+  // Destroying a recorded event is allowed; its resources go once it completes.
+  (void)hipEventDestroy(inputs_ready);
+  (void)hipEventDestroy(passing_ready);
+  return ok ? SPAVA_OK : SPAVA_ERR_HIP;
 }
 
 }  // extern "C"

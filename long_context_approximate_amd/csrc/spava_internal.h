@@ -49,6 +49,10 @@ void set_logit_store(Plan* p);
 // Dispatch order of the (block, query tile) pairs of the attention grid.
 enum ScheduleMode { kSchedLongestFirst = 0, kSchedNatural = 1, kSchedZigZag = 2 };
 
+// Which keys an attention launch covers: all of them, or the split parts X (whole
+// anchor tiles + local keys) and Y (the rest of the prefix, merged with X).
+enum AttnMode { kAttnFull = 0, kAttnPartX = 1, kAttnPartY = 2 };
+
 // Non-local prefix length of block h: anchor + passing rows of blocks 0..h-1.
 __host__ __device__ inline int prefix_len(const Plan& p, int h) {
   return h == 0 ? 0 : p.A + p.l0 + (h - 1) * p.l1;
@@ -59,7 +63,12 @@ struct SelectWs {
   size_t rowstat_part, rowstat, scores, logits, total;
 };
 struct AttnWs {
-  size_t kpre, vpre, vtloc, order, total;
+  size_t kpre, vpre, vtloc, order, order2, total;
+};
+
+// Workspace of the overlapped layer: selection, attention, and part X's (O, LSE).
+struct OverlapWs {
+  size_t select, attn, part_o, part_lse, total;
 };
 
 struct QueryWs {
@@ -69,6 +78,7 @@ struct QueryWs {
 SelectWs select_ws_layout(const Plan& p);
 AttnWs attn_ws_layout(const Plan& p);
 QueryWs query_ws_layout(const Plan& p, int64_t nq);
+OverlapWs overlap_ws_layout(const Plan& p);
 
 // Kernel launchers (defined next to their kernels). They return hipSuccess or the
 // launch error.
@@ -77,6 +87,16 @@ hipError_t launch_select(const Plan& p, const void* q, const void* k, int32_t* i
 hipError_t launch_attn_bf16(const Plan& p, const void* q, const void* k, const void* v,
                             const int32_t* idx, void* out, float* lse, char* ws,
                             hipStream_t st);
+// Split attention (bf16): part X needs no passing rows; the passing gather needs the
+// selection; part Y needs both and merges into out/lse.
+hipError_t launch_attn_bf16_part_x(const Plan& p, const void* q, const void* k, const void* v,
+                                   void* out, float* lse, char* ws, float* part_o,
+                                   float* part_lse, hipStream_t st);
+hipError_t launch_attn_bf16_gather_passing(const Plan& p, const void* k, const void* v,
+                                           const int32_t* idx, char* ws, hipStream_t st);
+hipError_t launch_attn_bf16_part_y(const Plan& p, const void* q, const void* k, void* out,
+                                   float* lse, char* ws, float* part_o, float* part_lse,
+                                   hipStream_t st);
 hipError_t launch_attn_f32(const Plan& p, const void* q, const void* k, const void* v,
                            const int32_t* idx, void* out, float* lse, char* ws,
                            hipStream_t st);

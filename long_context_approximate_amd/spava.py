@@ -30,6 +30,8 @@ EXPORTS = (
     "spava_query_attn_fwd",
     "spava_select_query_workspace_bytes",
     "spava_select_passing_query",
+    "spava_layer_overlap_workspace_bytes",
+    "spava_layer_overlap_fwd",
 )
 
 
@@ -101,6 +103,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.spava_select_query_workspace_bytes.restype = ctypes.c_int
     lib.spava_select_passing_query.argtypes = [shp, ctypes.c_int64, vp, vp, i32p, f64p, vp, sz, vp]
     lib.spava_select_passing_query.restype = ctypes.c_int
+    lib.spava_layer_overlap_workspace_bytes.argtypes = [shp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.spava_layer_overlap_workspace_bytes.restype = ctypes.c_int
+    lib.spava_layer_overlap_fwd.argtypes = [shp, vp, vp, vp, i32p, f64p, vp, f32p, vp, sz, vp, vp]
+    lib.spava_layer_overlap_fwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -220,6 +226,29 @@ def spava_query_attn_fwd(shape: SpavaShape, q_qr, k_qr, v_qr, k, v, out_qr, lse_
     _check(load().spava_query_attn_fwd(ctypes.byref(shape), n_query, _ptr(q_qr), _ptr(k_qr),
                                        _ptr(v_qr), _ptr(k), _ptr(v), _ptr(out_qr), _ptr(lse_qr),
                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return ws
+
+
+def spava_layer_overlap_workspace_bytes(shape: SpavaShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().spava_layer_overlap_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def spava_layer_overlap_fwd(shape: SpavaShape, q, k, v, passing_idx, out, lse_out=None,
+                            scores_out=None, workspace=None, stream=None, side_stream=None):
+    """Selection + attention of one layer, the selection on side_stream overlapped with
+    the passing-independent attention on stream."""
+    nbytes = spava_layer_overlap_workspace_bytes(shape)
+    ws = _workspace(nbytes, q.device, workspace)
+    main = _stream(stream)
+    side = side_stream.cuda_stream if side_stream is not None else None
+    if side is None:
+        raise ValueError("side_stream is required (a torch.cuda.Stream)")
+    _check(load().spava_layer_overlap_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(passing_idx), _ptr(scores_out), _ptr(out),
+                                          _ptr(lse_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                          main, side))
     return ws
 
 

@@ -103,7 +103,7 @@ def _expected_ws(sh):
     lpad = -(-lmax // 64) * 64
     attn = 2 * r(hkv * lpad * d * es)
     attn += r(hkv * H * (-(-nb // 64)) * 64 * d * es) if es == 2 else 0
-    attn += r(H * (-(-nb // 256)) * 4)
+    attn += 2 * r(H * (-(-nb // 256)) * 4)          # two schedule orders
     return sel, attn
 
 
@@ -193,6 +193,32 @@ def test_query_selection_entry_validation(lib):
     assert f(s, 100, FAKE, FAKE, None, None, FAKE, n.value, None) == ERR_NULL
     assert f(s, 100, FAKE, FAKE + 2, FAKE, None, FAKE, n.value, None) == ERR_ALIGN
     assert f(s, 100, FAKE, FAKE, FAKE, None, FAKE, n.value - 1, None) == ERR_WS
+
+
+def test_overlap_entry_workspace_and_validation(lib):
+    sh = _shape()
+    n = ctypes.c_size_t()
+    assert lib.spava_layer_overlap_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)) == OK
+    def r(b):
+        return (b + 255) // 256 * 256
+    sel, attn = _expected_ws(sh)
+    N, Hq, d = sh.seq_len, sh.num_q_heads, sh.head_dim
+    assert n.value == r(sel) + r(attn) + r(N * Hq * d * 4) + r(Hq * N * 4)
+    f = lib.spava_layer_overlap_fwd
+    s = ctypes.byref(sh)
+    ws = n.value
+    assert f(s, None, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, ws, None, None) == ERR_NULL
+    assert f(s, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, ws, None, None) == ERR_NULL
+    assert f(s, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, ws, None, None) == ERR_NULL
+    assert f(s, FAKE, FAKE, FAKE + 8, FAKE, None, FAKE, None, FAKE, ws, None, None) == ERR_ALIGN
+    assert f(s, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None, FAKE, ws, None, None) == ERR_ALIGN
+    assert f(s, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, ws - 1, None, None) == ERR_WS
+    f32 = _shape(dtype=1)
+    assert f(ctypes.byref(f32), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, ws, None,
+             None) == ERR_DTYPE
+    bad = _shape(seq_len=4095)
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, ws, None,
+             None) == ERR_SHAPE
 
 
 def test_status_strings(lib):

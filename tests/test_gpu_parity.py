@@ -243,6 +243,76 @@ def test_stored_and_recomputed_logits_agree_bitwise(monkeypatch, name):
                                              "scores": scores})
 
 
+# ---------------------------------- overlapped layer (selection beside part X)
+
+def _gpu_overlap(cfg, x):
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
+    idx = torch.full((max(H - 1, 0), hkv, l), -7, dtype=torch.int32, device="cuda")
+    scores = torch.full((max(H - 1, 0), hkv, nb), -1.0, dtype=torch.float64, device="cuda")
+    out = torch.full((cfg.seq_len, cfg.num_q_heads, cfg.head_dim), float("nan"),
+                     dtype=dev["q"].dtype, device="cuda")
+    lse = torch.full((cfg.num_q_heads, cfg.seq_len), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    side = torch.cuda.Stream()
+    spava.spava_layer_overlap_fwd(shape, dev["q"], dev["k"], dev["v"], idx, out, lse, scores,
+                                  side_stream=side)
+    torch.cuda.synchronize()
+    return {"idx": idx.cpu().numpy(), "scores": scores.cpu().numpy(),
+            "out": out.float().cpu().numpy(), "lse": lse.cpu().numpy()}
+
+
+OVERLAP = [
+    small_config(),                                                        # A = 100: ragged anchor tile
+    small_config(name="ov_anchor128", seq_len=2048, num_hosts=4, anchor_len=128, seed=61),
+    small_config(name="ov_d64", head_dim=64, seq_len=2048, num_hosts=4, num_q_heads=8,
+                 num_kv_heads=2, anchor_len=64, passing_len=128, window=64, seed=62),
+    small_config(name="ov_no_anchor", seq_len=1536, num_hosts=3, anchor_len=0, seed=63),
+    small_config(name="ov_no_pass", seq_len=1536, num_hosts=3, anchor_len=64, passing_len=0,
+                 seed=64),
+    small_config(name="ov_one_host", seq_len=1000, num_hosts=1, anchor_len=0, seed=65),
+    small_config(name="ov_pass_all", seq_len=1024, num_hosts=4, anchor_len=40, passing_len=300,
+                 seed=66),
+]
+
+
+@pytest.mark.parametrize("cfg", OVERLAP, ids=[c.name for c in OVERLAP])
+def test_overlap_layer_parity(cfg):
+    x = make_inputs(cfg)
+    got = _gpu_overlap(cfg, x)
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    _check_selection(cfg, got, ref)
+    _check_full(cfg, got, ref)
+    # Same selection as the two-call path, bitwise.
+    two, _ = _gpu_run(cfg, x)
+    assert np.array_equal(got["idx"], two["idx"])
+    assert np.array_equal(got["scores"], two["scores"])
+
+
+def test_overlap_layer_full_size_sampled_rows():
+    cfg = CONFIGS["h8_128k"]
+    x = make_inputs(cfg)
+    got = _gpu_overlap(cfg, x)
+    sh = oracle.shape_of(cfg)
+    scores = oracle.all_window_scores(sh, x["q"], x["k"])
+    ref_idx = oracle.select_passing(sh, scores)
+    _check_selection(cfg, got, {"idx": ref_idx, "scores": scores})
+    rng = np.random.default_rng(cfg.seed + 1)
+    worst_o = worst_l = 0.0
+    for rows in _sample_rows(cfg, rng):
+        rows = np.array(rows)
+        for hq in range(0, cfg.num_q_heads, 3):
+            o, lse = oracle.attention_rows(sh, x["q"], x["k"], x["v"], ref_idx, hq, rows)
+            worst_o = max(worst_o, float(np.abs(got["out"][rows, hq] - o).max()))
+            worst_l = max(worst_l, float(np.abs(got["lse"][hq, rows] - lse).max()))
+    assert worst_o <= 2e-2, f"max |dO| = {worst_o:.3e}"
+    assert worst_l <= 1e-3, f"max |dLSE| = {worst_l:.3e}"
+    assert np.isfinite(got["out"]).all() and np.isfinite(got["lse"]).all()
+
+
 # ------------------------------------------------------------- query block B_qr
 
 def _query_case(cfg, x, nq_take=None, context=None):
