@@ -203,6 +203,21 @@ def query_block_timing(cfg, shape, k, v, stream, n_query=256, reps=5):
             "query_aware_select_ms": sel_ms}
 
 
+def overlap_timing(shape, q, k, v, idx, out, lse, stream, t_step, reps=5):
+    """The same layer through the overlapped entry: selection + passing gather on a
+    side stream beside the passing-independent attention part (one-GPU form of the
+    pages' overlapped transfers)."""
+    import torch
+
+    from long_context_approximate_amd import spava
+    ws = torch.empty(spava.spava_layer_overlap_workspace_bytes(shape), dtype=torch.uint8,
+                     device="cuda")
+    side = torch.cuda.Stream()
+    ms = _time_call(lambda: spava.spava_layer_overlap_fwd(shape, q, k, v, idx, out, lse, None, ws,
+                                                          stream, side), stream, reps)
+    return {"step_ms": ms, "serial_step_ms": t_step * 1e3, "speedup": t_step * 1e3 / ms}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,7 +226,8 @@ def main():
     ap.add_argument("--workload", default="h8_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the dense (one host) baseline and the schedule comparison")
+                    help="skip the dense (one host) baseline, the schedule comparison, the "
+                         "query block and the overlapped layer")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -305,6 +321,7 @@ def main():
         rec["schedules_attn_ms"] = time_schedules(shape, q, k, v, idx, out, lse, ws_attn, stream)
         rec["dense_causal"] = dense_baseline(cfg, q, k, v, stream, t_step)
         rec["query_block"] = query_block_timing(cfg, shape, k, v, stream)
+        rec["overlap"] = overlap_timing(shape, q, k, v, idx, out, lse, stream, t_step)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, x)
     print(json.dumps(rec), flush=True)
