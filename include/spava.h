@@ -87,7 +87,10 @@ typedef enum { SPAVA_BF16 = 0, SPAVA_F32 = 1 } spava_dtype;
  *                                      C_0 = [A, n_b) and C_j = block j for j >= 1)
  *   1 <= window w <= n_b              (observer queries: the last w of each block)
  *   sm_scale: logit scale; <= 0 selects 1/sqrt(head_dim).
- *   N * max(Hq, Hkv) * head_dim < 2^31 is not required; offsets are 64-bit.
+ *   Offsets are 64-bit; the limits are those of the launches: Hq, Hkv <= 65535 and
+ *   every kernel grid below 2^31 work items, which for the attention means
+ *   N * Hq < 2^30 (e.g. 16M tokens x 32 heads), and for the selection
+ *   (H-1) * Hkv * ceil(G*w/32) * ceil(n_b/2048) * 64 < 2^31.
  * Alignment (else SPAVA_ERR_ALIGN): tensor pointers 16-byte aligned; strides a
  * multiple of 8 elements (bf16) or 4 elements (f32).
  */

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <mutex>
 
 #include "spava_internal.h"
@@ -17,6 +18,27 @@ static size_t region(size_t& cursor, size_t bytes) {
   size_t at = cursor;
   cursor += static_cast<size_t>(round_up(static_cast<int64_t>(bytes), 256));
   return at;
+}
+
+// The product of the factors (each in [0, 2^31)) is at most INT32_MAX, so a launch of
+// that many work items fits the 32-bit grid size of a dispatch and int indexing.
+// Stops at the first partial product above the bound, so nothing overflows.
+static bool fits_launch(std::initializer_list<int64_t> factors) {
+  int64_t prod = 1;
+  for (int64_t f : factors) {
+    if (f < 0 || f > INT32_MAX) return false;
+    prod *= f;
+    if (prod > INT32_MAX) return false;
+  }
+  return true;
+}
+
+// The selection's launches for this plan's observer count R.
+static bool select_launches_fit(const Plan& p) {
+  const int64_t j = p.H > 1 ? p.H - 1 : 0;
+  return fits_launch({j, p.Hkv, cdiv(p.R, 32), p.KS, 64}) &&
+         fits_launch({j, p.Hkv, cdiv(p.nb, 32), 64}) && fits_launch({j, p.Hkv, p.R}) &&
+         fits_launch({j, p.Hkv, 1024});
 }
 
 static spava_status make_plan(const spava_shape* s, Plan* p) {
@@ -76,6 +98,16 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   // longest first). Every order computes the same values; only timing differs.
   p->obs_query = 0;
   set_logit_store(p);
+  // Every launch must fit a 32-bit work-item count and the int arithmetic of its
+  // indexing. The attention grid bound also keeps N * Hq below 2^30.
+  if (p->Hq > 65535 || p->Hkv > 65535) return SPAVA_ERR_SHAPE;
+  if (!fits_launch({p->H, p->T, p->Hkv})) return SPAVA_ERR_SHAPE;
+  const int64_t attn_groups = round_up(static_cast<int64_t>(p->H) * p->T * p->Hkv, 8);
+  if (!fits_launch({attn_groups, p->G, 512})) return SPAVA_ERR_SHAPE;    // attention
+  if (!fits_launch({p->H, p->loc_tiles})) return SPAVA_ERR_SHAPE;
+  const int64_t prep_groups = p->Lpad / kKeyTile + static_cast<int64_t>(p->H) * p->loc_tiles;
+  if (!fits_launch({prep_groups, 256})) return SPAVA_ERR_SHAPE;           // gather
+  if (!select_launches_fit(*p)) return SPAVA_ERR_SHAPE;
   p->sched = kSchedLongestFirst;
   if (const char* e = getenv("SPAVA_SCHEDULE")) {
     if (strcmp(e, "natural") == 0) p->sched = kSchedNatural;
@@ -88,10 +120,13 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
 // storing them (less workspace, more time). Scores are bitwise the same either way.
 void set_logit_store(Plan* p) {
   const int64_t jg = static_cast<int64_t>(p->H > 1 ? p->H - 1 : 0) * p->Hkv;
-  const int64_t per_pair = static_cast<int64_t>(p->R) * p->nb * static_cast<int64_t>(sizeof(double));
   const char* e = getenv("SPAVA_SELECT_LOGITS");
   const bool recompute = e && strcmp(e, "recompute") == 0;
-  p->store_logits = (!recompute && jg > 0 && per_pair <= kLogitPairBytes) ? 1 : 0;
+  // R * nb * 8 <= kLogitPairBytes, tested without forming the (possibly huge) product.
+  const bool small = p->R <= kLogitPairBytes / (static_cast<int64_t>(sizeof(double)) * p->nb);
+  const int64_t per_pair =
+      small ? static_cast<int64_t>(p->R) * p->nb * static_cast<int64_t>(sizeof(double)) : 0;
+  p->store_logits = (!recompute && jg > 0 && small) ? 1 : 0;
   p->pair_chunk = p->store_logits
                       ? static_cast<int>(std::max<int64_t>(1, std::min(jg, kLogitChunkBytes / per_pair)))
                       : 0;
@@ -268,6 +303,13 @@ spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, cons
   return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
 }
 
+// The query block's launches: 1 <= n_query <= 2^30, partial and merge grids in range.
+static bool query_launches_fit(const Plan& p, int64_t nq) {
+  if (nq < 1 || nq > (int64_t(1) << 30)) return false;
+  return fits_launch({static_cast<int64_t>(p.H) + 1, cdiv(nq, kQTile), 512}) &&
+         fits_launch({nq, p.Hq, p.D / 4}) && fits_launch({cdiv(nq, kKeyTile), 256});
+}
+
 // Plan of the query-aware selection: observers are the n_query rows of a query block.
 static spava_status make_query_select_plan(const spava_shape* shape, int64_t n_query, Plan* p) {
   spava_status st = make_plan(shape, p);
@@ -277,6 +319,7 @@ static spava_status make_query_select_plan(const spava_shape* shape, int64_t n_q
   p->R = static_cast<int>(n_query * p->G);
   p->obs_query = 1;
   set_logit_store(p);
+  if (!select_launches_fit(*p)) return SPAVA_ERR_SHAPE;
   return SPAVA_OK;
 }
 
@@ -323,7 +366,7 @@ spava_status spava_query_workspace_bytes(const spava_shape* shape, int64_t n_que
   Plan p;
   spava_status st = make_plan(shape, &p);
   if (st != SPAVA_OK) return st;
-  if (n_query < 1 || n_query > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
+  if (!query_launches_fit(p, n_query)) return SPAVA_ERR_SHAPE;
   *bytes = query_ws_layout(p, n_query).total;
   return SPAVA_OK;
 }
@@ -335,7 +378,7 @@ spava_status spava_query_attn_fwd(const spava_shape* shape, int64_t n_query, con
   Plan p;
   spava_status st = make_plan(shape, &p);
   if (st != SPAVA_OK) return st;
-  if (n_query < 1 || n_query > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
+  if (!query_launches_fit(p, n_query)) return SPAVA_ERR_SHAPE;
   if (!q_qr || !k_qr || !v_qr || !k || !v || !out_qr || !workspace) return SPAVA_ERR_NULL;
   if (!aligned16(q_qr) || !aligned16(k_qr) || !aligned16(v_qr) || !aligned16(k) ||
       !aligned16(v) || !aligned16(out_qr) || !aligned16(workspace))
