@@ -243,6 +243,39 @@ def test_stored_and_recomputed_logits_agree_bitwise(monkeypatch, name):
                                              "scores": scores})
 
 
+def test_workspace_contents_do_not_matter():
+    # Workspaces filled with zeros and with 0xFF bytes (NaN patterns in every float
+    # view) must give bitwise-equal results: nothing reads scratch it has not written.
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    cfg = small_config(name="poison", seq_len=3000, num_hosts=3, seed=71)
+    x = make_inputs(cfg)
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
+    results = []
+    for fill in (0x00, 0xFF):
+        def ws(nbytes):
+            return torch.full((max(nbytes, 1),), fill, dtype=torch.uint8, device="cuda")
+        idx = torch.empty((H - 1, hkv, l), dtype=torch.int32, device="cuda")
+        sc = torch.empty((H - 1, hkv, nb), dtype=torch.float64, device="cuda")
+        out = torch.empty((cfg.seq_len, cfg.num_q_heads, cfg.head_dim), dtype=dev["q"].dtype,
+                          device="cuda")
+        lse = torch.empty((cfg.num_q_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+        spava.spava_select_passing(shape, dev["q"], dev["k"], idx, sc,
+                                   ws(spava.spava_select_workspace_bytes(shape)))
+        spava.spava_approx_attn_fwd(shape, dev["q"], dev["k"], dev["v"], idx, out, lse,
+                                    ws(spava.spava_attn_workspace_bytes(shape)))
+        out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+        spava.spava_layer_overlap_fwd(shape, dev["q"], dev["k"], dev["v"], idx, out2, lse2,
+                                      workspace=ws(spava.spava_layer_overlap_workspace_bytes(shape)),
+                                      side_stream=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        results.append([t.cpu() for t in (idx, sc, out.float(), lse, out2.float(), lse2)])
+    for a, b in zip(*results):
+        assert torch.equal(a, b)
+
+
 # ---------------------------------- overlapped layer (selection beside part X)
 
 def _gpu_overlap(cfg, x):
