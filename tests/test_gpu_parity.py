@@ -195,6 +195,10 @@ def test_full_size_selection_and_sampled_rows(name):
     got, x = _gpu_run(cfg)
     sh = oracle.shape_of(cfg)
     scores = oracle.all_window_scores(sh, x["q"], x["k"])
+    # Every boundary decision must be decidable at fp64: the relative gap between the
+    # last selected and the first rejected score far above the scores' 1e-12 bar.
+    margins = oracle.selection_margins(sh, scores)
+    assert np.nanmin(margins) > 1e-10, f"undecidable at fp64: margin {np.nanmin(margins):.2e}"
     ref_idx = oracle.select_passing(sh, scores)
     _check_selection(cfg, got, {"idx": ref_idx, "scores": scores})
     rng = np.random.default_rng(cfg.seed)
