@@ -280,6 +280,52 @@ def test_workspace_contents_do_not_matter():
         assert torch.equal(a, b)
 
 
+def test_layer_replays_from_a_hip_graph():
+    # The library only enqueues kernels (no allocation, no memset), so a layer can be
+    # captured once and replayed. Every replay, with eager work and synchronisation in
+    # between, must match the eager result bitwise.
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    cfg = small_config(name="graph", seq_len=3000, num_hosts=3, seed=72)
+    x = make_inputs(cfg)
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
+    ws_s = torch.empty(spava.spava_select_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(spava.spava_attn_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((H - 1, hkv, l), dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.seq_len, cfg.num_q_heads, cfg.head_dim), dtype=dev["q"].dtype,
+                      device="cuda")
+    lse = torch.empty((cfg.num_q_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+
+    def layer():
+        spava.spava_select_passing(shape, dev["q"], dev["k"], idx, None, ws_s)
+        spava.spava_approx_attn_fwd(shape, dev["q"], dev["k"], dev["v"], idx, out, lse, ws_a)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()                                   # eager reference, off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (idx, out, lse)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    for rep in range(3):
+        for t in (idx, out, lse):
+            t.zero_()                             # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((idx, out, lse), ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+    got = {"idx": idx.cpu().numpy(), "out": out.float().cpu().numpy(), "lse": lse.cpu().numpy()}
+    r = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    assert np.array_equal(got["idx"], r["idx"])
+    _check_full(cfg, got, r)
+
+
 # ---------------------------------- overlapped layer (selection beside part X)
 
 def _gpu_overlap(cfg, x):
