@@ -133,9 +133,10 @@ __device__ inline int pair_cost(const Plan& p, int pair, int mode) {
 // paired as (p, H-1-p), the pages' host pairing, tiles of a pair alternating.
 __global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restrict__ order,
                                                        int mode) {
+  __shared__ int cost[256];
   const int P = p.H * p.T;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= P) return;
+  const bool valid = i < P;
   int rank = 0;
   if (p.sched == kSchedNatural) {
     rank = i;
@@ -145,22 +146,32 @@ __global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restri
     const int pr = min(h, mirror);
     rank = (h == mirror) ? pr * 2 * p.T + t : pr * 2 * p.T + 2 * t + (h > mirror ? 1 : 0);
   } else {
-    const int ci = pair_cost(p, i, mode);
-    for (int j = 0; j < P; ++j) {
-      const int cj = pair_cost(p, j, mode);
-      rank += (cj > ci) || (cj == ci && j < i);
+    // Rank = number of pairs that come first (higher cost, or equal cost and lower
+    // index); the costs of each chunk of 256 pairs are computed once into LDS.
+    const int ci = valid ? pair_cost(p, i, mode) : 0;
+    for (int j0 = 0; j0 < P; j0 += 256) {
+      __syncthreads();
+      if (j0 + static_cast<int>(threadIdx.x) < P)
+        cost[threadIdx.x] = pair_cost(p, j0 + threadIdx.x, mode);
+      __syncthreads();
+      const int n = min(256, P - j0);
+      for (int jj = 0; jj < n; ++jj) {
+        const int cj = cost[jj];
+        rank += (cj > ci) || (cj == ci && j0 + jj < i);
+      }
     }
   }
-  order[rank] = i;
+  if (valid) order[rank] = i;
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void attn_kernel(
     Plan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kpre, const uint16_t* __restrict__ vtpre,
     const uint16_t* __restrict__ vtloc, const int32_t* __restrict__ order,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int NG, float c_log2, int mode,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int NG, float c_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
+  constexpr int mode = MODE;
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
 
@@ -335,9 +346,16 @@ void launch_attn_mode(const Plan& p, const uint16_t* q, const uint16_t* k, const
   const int NG = P * p.Hkv;
   const int64_t grid = round_up(NG, 8) * p.G;
   const float c_log2 = static_cast<float>(p.scale * 1.4426950408889634);
-  hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p, q,
-                     k, a.kpre, a.vtpre, a.vtloc, order, out, lse, NG, c_log2, mode, part_o,
-                     part_lse);
+  const dim3 gd(static_cast<unsigned>(grid));
+  if (mode == kAttnPartX)
+    hipLaunchKernelGGL((attn_kernel<D, kAttnPartX>), gd, dim3(kThreads), 0, st, p, q, k, a.kpre,
+                       a.vtpre, a.vtloc, order, out, lse, NG, c_log2, part_o, part_lse);
+  else if (mode == kAttnPartY)
+    hipLaunchKernelGGL((attn_kernel<D, kAttnPartY>), gd, dim3(kThreads), 0, st, p, q, k, a.kpre,
+                       a.vtpre, a.vtloc, order, out, lse, NG, c_log2, part_o, part_lse);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, kAttnFull>), gd, dim3(kThreads), 0, st, p, q, k, a.kpre,
+                       a.vtpre, a.vtloc, order, out, lse, NG, c_log2, part_o, part_lse);
 }
 
 template <int D>
