@@ -159,6 +159,32 @@ __device__ inline void load_keys(const Plan& p, const T* k, int g, int64_t key0,
   }
 }
 
+// exp(y) for y <= 0 in float64, within 2 ulp. Every exponent on the hot paths is a
+// logit minus a running or final row maximum, so it is never positive. Tang's
+// table-driven method: y = (64 n + j) ln2/64 + r with |r| <= ln2/128, so
+// exp(y) = 2^n * 2^(j/64) * exp(r); 2^(j/64) comes from a 64-entry table in LDS and
+// exp(r) from its degree-5 Taylor polynomial (truncation error below 2^-60). ln2/64 is
+// split into a 36-bit head (exact products k * head for |k| < 2^17) and a tail.
+// Arguments below -745.2 underflow to 0.
+constexpr int kExpTab = 64;
+__device__ inline void init_exp_table(double* tab) {
+  if (threadIdx.x < kExpTab) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) / kExpTab);
+  __syncthreads();
+}
+__device__ inline double exp_nonpos(double y, const double* tab) {
+  if (!(y > -745.2)) return 0.0;
+  const double k = rint(y * 0x1.71547652b82fep+6);          // y * 64 / ln2
+  double r = fma(-k, 0x1.62e42fefa0000p-7, y);              // head of ln2 / 64
+  r = fma(-k, 0x1.cf79abc9e3b3ap-46, r);                    // tail
+  double a = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  a = fma(r, a, 1.0 / 6.0);
+  a = fma(r, a, 0.5);
+  a = fma(r, a, 1.0);
+  const double er = fma(r, a, 1.0);
+  const int ki = static_cast<int>(k);
+  return ldexp(tab[ki & (kExpTab - 1)] * er, ki >> 6);
+}
+
 // Combine two (max, sum) pairs of the same row.
 __device__ inline void lse_merge(double& m, double& z, double mo, double zo) {
   const double mn = fmax(m, mo);
@@ -178,6 +204,8 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
                                                        double2* __restrict__ part,
                                                        double* __restrict__ logits,
                                                        int row_tiles, int jg0, int npairs) {
+  __shared__ double etab[kExpTab];
+  init_exp_table(etab);
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t total = static_cast<int64_t>(npairs) * row_tiles * p.KS;
   if (wid >= total) return;
@@ -233,12 +261,12 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
             lg[static_cast<int64_t>(r0 + rb * 16 + 4 * rr + kg) * p.nb + (key - s)] = x[kb];
         }
         if (mt > m[rb][rr]) {
-          z[rb][rr] = (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp(m[rb][rr] - mt);
+          z[rb][rr] = (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp_nonpos(m[rb][rr] - mt, etab);
           m[rb][rr] = mt;
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          if (vis[kb]) z[rb][rr] += exp(x[kb] - m[rb][rr]);
+          if (vis[kb]) z[rb][rr] += exp_nonpos(x[kb] - m[rb][rr], etab);
       }
   }
   // Reduce over the 16 lanes (l % 16) that hold different keys of the same rows.
@@ -277,8 +305,8 @@ __global__ void merge_kernel(Plan p, const double2* __restrict__ part,
 }
 
 // exp(x - m) / z of one visible (row, key), else 0 (the same code in both score passes).
-__device__ inline double prob_term(bool vis, double x, double2 mz) {
-  return vis ? exp(x - mz.x) * mz.y : 0.0;
+__device__ inline double prob_term(bool vis, double x, double2 mz, const double* etab) {
+  return vis ? exp_nonpos(x - mz.x, etab) * mz.y : 0.0;
 }
 
 // The four lanes col, col+16, col+32, col+48 hold disjoint row sets of the same key;
@@ -306,6 +334,8 @@ __global__ __launch_bounds__(256) void colsum_kernel(Plan p, const T* __restrict
                                                      const T* __restrict__ k,
                                                      const double2* __restrict__ rowstat,
                                                      double* __restrict__ scores, int key_tiles) {
+  __shared__ double etab[kExpTab];
+  init_exp_table(etab);
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t total = static_cast<int64_t>(p.H - 1) * p.Hkv * key_tiles;
   if (wid >= total) return;
@@ -345,7 +375,7 @@ __global__ __launch_bounds__(256) void colsum_kernel(Plan p, const T* __restrict
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const double x = p.scale * acc[rb][kb][rr];
-          colsum[kb] += prob_term(key[kb] <= qi, x, mz);
+          colsum[kb] += prob_term(key[kb] <= qi, x, mz, etab);
         }
       }
   }
@@ -359,6 +389,8 @@ __global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double
                                                             const double2* __restrict__ rowstat,
                                                             double* __restrict__ scores,
                                                             int key_tiles, int jg0, int npairs) {
+  __shared__ double etab[kExpTab];
+  init_exp_table(etab);
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t total = static_cast<int64_t>(npairs) * key_tiles;
   if (wid >= total) return;
@@ -389,7 +421,7 @@ __global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double
         for (int kb = 0; kb < 2; ++kb) {
           const bool vis = key[kb] <= qi && key[kb] < e;
           const double x = vis ? lg[static_cast<int64_t>(r) * p.nb + (key[kb] - s)] : 0.0;
-          colsum[kb] += prob_term(vis, x, mz);
+          colsum[kb] += prob_term(vis, x, mz, etab);
         }
       }
   }
