@@ -401,9 +401,13 @@ __global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double
   const int64_t s = static_cast<int64_t>(j) * p.nb;
   const int64_t e = s + p.nb;
   const int64_t key0 = s + static_cast<int64_t>(kt) * kWaveKeys;
+  // This lane holds two adjacent keys (one 16-byte load per row when both are
+  // visible and the rows are 16-byte aligned); the row order of every key's sum is
+  // that of colsum_kernel, so the scores are the same.
   int64_t key[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) key[kb] = key0 + kb * 16 + col;
+  for (int kb = 0; kb < 2; ++kb) key[kb] = key0 + 2 * col + kb;
+  const bool pairs16 = (p.nb & 1) == 0;
   const double2* st = rowstat + static_cast<int64_t>(jg) * p.R;
   const double* lg = logits + static_cast<int64_t>(jg - jg0) * p.R * p.nb;
 
@@ -417,12 +421,20 @@ __global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double
         const bool ok = r < p.R;
         const double2 mz = ok ? st[r] : make_double2(0.0, 0.0);
         const int64_t qi = ok ? row_key_limit(p, j, r) : -1;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bool vis = key[kb] <= qi && key[kb] < e;
-          const double x = vis ? lg[static_cast<int64_t>(r) * p.nb + (key[kb] - s)] : 0.0;
-          colsum[kb] += prob_term(vis, x, mz, etab);
+        const bool v0 = key[0] <= qi && key[0] < e;
+        const bool v1 = key[1] <= qi && key[1] < e;   // implies v0
+        const double* row = lg + static_cast<int64_t>(r) * p.nb + (key[0] - s);
+        double x0 = 0.0, x1 = 0.0;
+        if (v1 && pairs16) {
+          const double2 t = *reinterpret_cast<const double2*>(row);
+          x0 = t.x;
+          x1 = t.y;
+        } else {
+          if (v0) x0 = row[0];
+          if (v1) x1 = row[1];
         }
+        colsum[0] += prob_term(v0, x0, mz, etab);
+        colsum[1] += prob_term(v1, x1, mz, etab);
       }
   }
   finish_colsum(p, colsum, key, col, kg, jg, s, e, scores);
