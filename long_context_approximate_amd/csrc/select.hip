@@ -234,6 +234,16 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
       const int r = r0 + rb * 16 + 4 * rr + kg;
       qi[rb][rr] = r < p.R ? row_key_limit(p, j, r) : -1;   // -1: padding row sees nothing
     }
+  // Last key every row of this wave sees (wave-uniform); tiles at or below it, inside
+  // the split and without padding rows take the unmasked path.
+  int64_t qmin = INT64_MAX;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) qmin = min(qmin, qi[rb][rr]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) qmin = min(qmin, __shfl_xor(qmin, off));
+  const bool rows_full = r0 + kWaveRows <= p.R;
   Frag<T, D> kf[2];
   load_keys<T, D>(p, k, g, split_lo, split_hi, col, kg, kf);
   for (int64_t key0 = split_lo; key0 < split_hi; key0 += kWaveKeys) {
@@ -244,6 +254,30 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
     // Prefetch the next key tile while this tile's softmax statistics are formed.
     if (key0 + kWaveKeys < split_hi)
       load_keys<T, D>(p, k, g, key0 + kWaveKeys, split_hi, col, kg, kf);
+    const bool full = rows_full && key0 + kWaveKeys <= split_hi && key0 + kWaveKeys - 1 <= qmin;
+    if (full) {
+      // Every (row, key) of the tile is visible: the same updates without masks.
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const double x0 = p.scale * acc[rb][0][rr], x1 = p.scale * acc[rb][1][rr];
+          if (STORE) {
+            double* row = lg + static_cast<int64_t>(r0 + rb * 16 + 4 * rr + kg) * p.nb + (key0 - s);
+            row[col] = x0;
+            row[16 + col] = x1;
+          }
+          const double mt = fmax(x0, x1);
+          if (mt > m[rb][rr]) {
+            z[rb][rr] =
+                (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp_nonpos(m[rb][rr] - mt, etab);
+            m[rb][rr] = mt;
+          }
+          z[rb][rr] += exp_nonpos(x0 - m[rb][rr], etab);
+          z[rb][rr] += exp_nonpos(x1 - m[rb][rr], etab);
+        }
+      continue;
+    }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
