@@ -445,8 +445,26 @@ __global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double
   const double2* st = rowstat + static_cast<int64_t>(jg) * p.R;
   const double* lg = logits + static_cast<int64_t>(jg - jg0) * p.R * p.nb;
 
+  // Keys every observer row sees (window rows sit at e - w .. e - 1 and see keys up
+  // to their own position; query-block rows see the whole block): row tiles without
+  // padding rows then need no visibility test.
+  const bool keys_full = p.obs_query ? key0 + kWaveKeys <= e : key0 + kWaveKeys - 1 <= e - p.w;
   double colsum[2] = {0.0, 0.0};
   for (int r0 = 0; r0 < p.R; r0 += kWaveRows) {
+    if (keys_full && pairs16 && r0 + kWaveRows <= p.R) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = r0 + rb * 16 + 4 * rr + kg;
+          const double2 mz = st[r];
+          const double2 t =
+              *reinterpret_cast<const double2*>(lg + static_cast<int64_t>(r) * p.nb + (key[0] - s));
+          colsum[0] += prob_term(true, t.x, mz, etab);
+          colsum[1] += prob_term(true, t.y, mz, etab);
+        }
+      continue;
+    }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
