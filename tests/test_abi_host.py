@@ -225,3 +225,21 @@ def test_status_strings(lib):
     for code in range(8):
         assert spava.status_string(code).startswith("SPAVA")
     assert "unknown" in spava.status_string(42)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # There is no CPU fallback: without the built library every call raises.
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from long_context_approximate_amd import spava\n"
+            "try:\n"
+            "    spava.spava_select_workspace_bytes(spava.make_shape(4096, 4, 8, 2, 128, 128, 64, 32))\n"
+            "except FileNotFoundError as e:\n"
+            "    print('raised:', e)\n"
+            "    raise SystemExit(0)\n"
+            "raise SystemExit(1)\n" % ROOT)
+    env = dict(os.environ, SPAVA_LIB=str(tmp_path / "absent.so"))
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "is not built" in res.stdout
