@@ -81,6 +81,12 @@ SMALL = [
     small_config(name="G7_tail", seq_len=2600, num_hosts=2, num_q_heads=7, num_kv_heads=1,
                  anchor_len=1, passing_len=513, window=129, seed=11),
     small_config(name="t3_keys", seq_len=2048, num_hosts=4, dist="student_t3", seed=12),
+    # MHA (G = 1) with an odd head count, five hosts, a one-query window.
+    small_config(name="mha_h5_w1", seq_len=3500, num_hosts=5, num_q_heads=3, num_kv_heads=3,
+                 anchor_len=64, passing_len=200, window=1, seed=13),
+    # The window is the whole block; d = 64, G = 4, one KV head.
+    small_config(name="wfull_d64", seq_len=2048, num_hosts=4, num_q_heads=4, num_kv_heads=1,
+                 head_dim=64, anchor_len=32, passing_len=100, window=512, seed=14),
     CONFIGS["tiny_f32_512"],
 ]
 
