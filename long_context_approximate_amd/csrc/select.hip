@@ -186,11 +186,11 @@ __device__ inline double exp_nonpos(double y, const double* tab) {
 }
 
 // Combine two (max, sum) pairs of the same row.
-__device__ inline void lse_merge(double& m, double& z, double mo, double zo) {
+__device__ inline void lse_merge(double& m, double& z, double mo, double zo, const double* tab) {
   const double mn = fmax(m, mo);
   if (mn == -INFINITY) return;  // both empty
-  const double a = (m == -INFINITY) ? 0.0 : z * exp(m - mn);
-  const double b = (mo == -INFINITY) ? 0.0 : zo * exp(mo - mn);
+  const double a = (m == -INFINITY) ? 0.0 : z * exp_nonpos(m - mn, tab);
+  const double b = (mo == -INFINITY) ? 0.0 : zo * exp_nonpos(mo - mn, tab);
   z = a + b;
   m = mn;
 }
@@ -216,8 +216,8 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
   const int j = jg / p.Hkv, g = jg % p.Hkv;
   const int lane = threadIdx.x & 63, col = lane & 15, kg = lane >> 4;
   const int64_t s = static_cast<int64_t>(j) * p.nb;
-  const int64_t split_lo = s + static_cast<int64_t>(split) * kScoreSplitKeys;
-  const int64_t split_hi = min(s + p.nb, split_lo + kScoreSplitKeys);
+  const int64_t split_lo = s + static_cast<int64_t>(split) * p.split_keys;
+  const int64_t split_hi = min(s + p.nb, split_lo + p.split_keys);
   const int r0 = rt * kWaveRows;
   double* lg = STORE ? logits + static_cast<int64_t>(jg - jg0) * p.R * p.nb : nullptr;
 
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
       for (int off = 8; off >= 1; off >>= 1) {
         const double mo = __shfl_xor(m[rb][rr], off);
         const double zo = __shfl_xor(z[rb][rr], off);
-        lse_merge(m[rb][rr], z[rb][rr], mo, zo);
+        lse_merge(m[rb][rr], z[rb][rr], mo, zo, etab);
       }
       const int r = r0 + rb * 16 + 4 * rr + kg;
       if (col == 0 && r < p.R)
@@ -324,6 +324,8 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
 // Rows of the pairs [jg0, jg0 + npairs).
 __global__ void merge_kernel(Plan p, const double2* __restrict__ part,
                              double2* __restrict__ rowstat, int jg0, int npairs) {
+  __shared__ double etab[kExpTab];
+  init_exp_table(etab);
   const int64_t total = static_cast<int64_t>(npairs) * p.R;
   const int64_t t = static_cast<int64_t>(jg0) * p.R + static_cast<int64_t>(blockIdx.x) * blockDim.x +
                     threadIdx.x;
@@ -333,7 +335,7 @@ __global__ void merge_kernel(Plan p, const double2* __restrict__ part,
   double m = -INFINITY, z = 0.0;
   for (int sidx = 0; sidx < p.KS; ++sidx) {
     const double2 pr = part[(jg * p.KS + sidx) * p.R + r];
-    lse_merge(m, z, pr.x, pr.y);
+    lse_merge(m, z, pr.x, pr.y, etab);
   }
   rowstat[t] = make_double2(m, 1.0 / z);   // (max, 1 / sum)
 }

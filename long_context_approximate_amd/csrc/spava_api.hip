@@ -91,13 +91,12 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   const int64_t R = static_cast<int64_t>(p->G) * p->w;
   if (R > (int64_t(1) << 30)) return SPAVA_ERR_SHAPE;
   p->R = static_cast<int>(R);
-  p->KS = static_cast<int>(cdiv(nb, kScoreSplitKeys));
   p->T = static_cast<int>(cdiv(nb, kQTile));
   p->loc_tiles = static_cast<int>(cdiv(nb, kKeyTile));
   // SPAVA_SCHEDULE=lpt|natural|zigzag picks the attention dispatch order (default:
   // longest first). Every order computes the same values; only timing differs.
   p->obs_query = 0;
-  set_logit_store(p);
+  set_select_layout(p);
   // Every launch must fit a 32-bit work-item count and the int arithmetic of its
   // indexing. The attention grid bound also keeps N * Hq below 2^30.
   if (p->Hq > 65535 || p->Hkv > 65535) return SPAVA_ERR_SHAPE;
@@ -116,10 +115,29 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   return SPAVA_OK;
 }
 
-// SPAVA_SELECT_LOGITS=recompute makes the score pass recompute the logits instead of
-// storing them (less workspace, more time). Scores are bitwise the same either way.
-void set_logit_store(Plan* p) {
+// The selection's key split length (see kScoreSplitMin) and whether its score pass
+// reads stored logits. SPAVA_SELECT_LOGITS=recompute makes that pass recompute them
+// instead (less workspace, more time). Scores are bitwise the same either way: the
+// split length depends on the pair count of the whole call, not on the chunks.
+void set_select_layout(Plan* p) {
   const int64_t jg = static_cast<int64_t>(p->H > 1 ? p->H - 1 : 0) * p->Hkv;
+  const int64_t row_tiles = cdiv(p->R, 32);
+  // Past 2^31 (pair, row tile) units the launch check rejects the shape anyway; skip
+  // the search there so no product below can overflow.
+  const bool huge = jg > INT32_MAX || row_tiles > INT32_MAX / std::max<int64_t>(1, jg);
+  const int64_t units = std::max<int64_t>(1, huge ? 1 : jg * row_tiles);
+  int64_t best_cost = INT64_MAX;
+  p->split_keys = kScoreSplitMax;
+  for (int split = kScoreSplitMax; !huge && split >= kScoreSplitMin; split -= 32) {
+    const int64_t ks = cdiv(p->nb, split);
+    const int64_t cost = cdiv(units * ks, kScoreWaveSlots) *
+                         (std::min<int64_t>(split, p->nb) + kScoreWaveOverhead);
+    if (cost < best_cost) {
+      best_cost = cost;
+      p->split_keys = split;
+    }
+  }
+  p->KS = static_cast<int>(cdiv(p->nb, p->split_keys));
   const char* e = getenv("SPAVA_SELECT_LOGITS");
   const bool recompute = e && strcmp(e, "recompute") == 0;
   // R * nb * 8 <= kLogitPairBytes, tested without forming the (possibly huge) product.
@@ -318,7 +336,7 @@ static spava_status make_query_select_plan(const spava_shape* shape, int64_t n_q
   p->w = static_cast<int>(n_query);
   p->R = static_cast<int>(n_query * p->G);
   p->obs_query = 1;
-  set_logit_store(p);
+  set_select_layout(p);
   if (!select_launches_fit(*p)) return SPAVA_ERR_SHAPE;
   return SPAVA_OK;
 }

@@ -10,8 +10,16 @@ namespace spava {
 
 constexpr int kKeyTile = 64;     // keys per LDS tile in the attention kernels
 constexpr int kQTile = 256;      // queries per attention workgroup (8 waves x 32)
-constexpr int kScoreTile = 64;   // rows and keys per fp64 score workgroup tile
-constexpr int kScoreSplitKeys = 2048;  // keys per split in the row-statistics pass
+// Key splits of the row-statistics pass: one wave per (pair, 32 observer rows, split),
+// all of about the same cost. The waves resident on a SIMD share its matrix unit, so
+// the pass takes about ceil(waves / kScoreWaveSlots) * (split + kScoreWaveOverhead)
+// key steps, kScoreWaveSlots = 256 CUs x 4 SIMDs (a fit to timings of split lengths
+// 512..2048 at 16384 keys per block). The split length, a multiple of 32 in
+// [kScoreSplitMin, kScoreSplitMax], minimises that estimate (ties: the longer).
+constexpr int kScoreSplitMin = 512;
+constexpr int kScoreSplitMax = 4096;
+constexpr int kScoreWaveSlots = 1024;
+constexpr int kScoreWaveOverhead = 32;
 // The score pass keeps the float64 logits of the row-statistics pass when one
 // (block, KV head) pair's logits fit in kLogitPairBytes; pairs are then processed in
 // chunks of at most kLogitChunkBytes of logits. Otherwise the logits are recomputed.
@@ -33,7 +41,8 @@ struct Plan {
   int Lmax;         // non-local (anchor + passing) rows of the last block
   int Lpad;         // Lmax rounded up to a key tile
   int R;            // observer rows per (block, KV head): G * w
-  int KS;           // key splits of the row-statistics pass
+  int split_keys;   // keys per split of the row-statistics pass
+  int KS;           // key splits of the row-statistics pass: ceil(nb / split_keys)
   int T;            // query tiles per block
   int loc_tiles;    // key tiles per block
   int sched;        // query-tile dispatch order (ScheduleMode); never changes results
@@ -43,8 +52,8 @@ struct Plan {
   int pair_chunk;   // (block, KV head) pairs per chunk when logits are stored
 };
 
-// Decide whether the selection stores its logits (after R is final).
-void set_logit_store(Plan* p);
+// The selection's key splits and whether it stores its logits (after R is final).
+void set_select_layout(Plan* p);
 
 // Dispatch order of the (block, query tile) pairs of the attention grid.
 enum ScheduleMode { kSchedLongestFirst = 0, kSchedNatural = 1, kSchedZigZag = 2 };

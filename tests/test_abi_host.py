@@ -87,6 +87,29 @@ def _logit_bytes(jg, R, nb):
     return max(1, min(jg, (4 << 30) // per_pair)) * per_pair
 
 
+def _split_keys(jg, R, nb):
+    """Row-statistics key split: the multiple of 32 in [512, 4096] that minimises
+    ceil(waves / 1024) * (split + 32), waves = pairs * ceil(R / 32) * ceil(nb / split);
+    ties to the longer split."""
+    units = max(1, jg * -(-R // 32))
+    best = None
+    for split in range(4096, 511, -32):
+        cost = -(-units * -(-nb // split) // 1024) * (min(split, nb) + 32)
+        if best is None or cost < best[0]:
+            best = (cost, split)
+    return best[1]
+
+
+def test_split_keys_balance_the_row_statistics_waves():
+    # 28 pairs x 28 row tiles at 16384 keys per block: 2048-key splits give 6272 waves,
+    # 6.1 per SIMD (a seventh, nearly empty round); 1824-key splits 7056 waves, 6.9.
+    assert _split_keys(28, 896, 16384) == 1824
+    # 120 pairs x 16 row tiles: 2048-key splits give exactly 15 waves per SIMD.
+    assert _split_keys(120, 512, 16384) == 2048
+    # Few waves: the shortest split gives the most parallel waves.
+    assert _split_keys(2, 64, 8192) == 512
+
+
 def _expected_ws(sh):
     def r(b):
         return (b + 255) // 256 * 256
@@ -94,8 +117,8 @@ def _expected_ws(sh):
         sh.window, sh.head_dim
     nb = sh.seq_len // H
     es = 2 if sh.dtype == spava.SPAVA_BF16 else 4
-    ks = -(-nb // 2048)
     jg = (H - 1) * hkv
+    ks = -(-nb // _split_keys(jg, G * w, nb))
     sel = r(jg * ks * G * w * 16) + r(jg * G * w * 16) + r(jg * nb * 8) + r(_logit_bytes(jg, G * w, nb))
     l0 = min(sh.passing_len, nb - sh.anchor_len) if H > 1 else 0
     l1 = min(sh.passing_len, nb) if H > 2 else 0
@@ -185,7 +208,8 @@ def test_query_selection_entry_validation(lib):
     def r(b):
         return (b + 255) // 256 * 256
     jg, R = 3 * 2, 4 * 100
-    assert n.value == (r(jg * 1 * R * 16) + r(jg * R * 16) + r(jg * 1024 * 8)
+    ks = -(-1024 // _split_keys(jg, R, 1024))
+    assert n.value == (r(jg * ks * R * 16) + r(jg * R * 16) + r(jg * 1024 * 8)
                        + r(_logit_bytes(jg, R, 1024)))
     f = lib.spava_select_passing_query
     s = ctypes.byref(sh)
