@@ -90,7 +90,10 @@ typedef enum { SPAVA_BF16 = 0, SPAVA_F32 = 1 } spava_dtype;
  *   Offsets are 64-bit; the limits are those of the launches: Hq, Hkv <= 65535 and
  *   every kernel grid below 2^31 work items, which for the attention means
  *   N * Hq < 2^30 (e.g. 16M tokens x 32 heads), and for the selection
- *   (H-1) * Hkv * ceil(G*w/32) * ceil(n_b/2048) * 64 < 2^31.
+ *   (H-1) * Hkv * ceil(G*w/32) * S * 64 < 2^31, S = ceil(n_b / split) key splits of
+ *   the row statistics (split between 512 and 4096 keys, chosen per shape).
+ *   kv_stride_tok <= 17043519 elements: attention reads K tiles in place through
+ *   32-bit buffer offsets (63 token strides plus one row below 2^31 bytes).
  * Alignment (else SPAVA_ERR_ALIGN): tensor pointers 16-byte aligned; strides a
  * multiple of 8 elements (bf16) or 4 elements (f32).
  */

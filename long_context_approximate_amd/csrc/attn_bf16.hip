@@ -213,18 +213,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
 
   // Tile it: prefix tiles come from the gathered Kpre/Vtpre, local tiles read K in
   // place and V^T from the block's transposed tiles.
-  TileStage<D> stage;
-  auto load_tile = [&](int it) {
+  TileDma<D> dma;
+  dma.init(p.kvs_tok);
+  auto issue_tile = [&](int it, char* dst) {
     const bool pre = it < np;
     const int pt = tr.pt0 + it;
     const int lt = it - np;
     const int64_t key0 = s_h + static_cast<int64_t>(lt) * BN;
     const uint16_t* kb = pre ? kpre_g + static_cast<int64_t>(pt) * BN * D : k_g + key0 * p.kvs_tok;
-    const int64_t krow = pre ? D : p.kvs_tok;
     const int64_t kvalid = pre ? BN : e_h - key0;
     const uint16_t* vb = pre ? vtpre_g + static_cast<int64_t>(pt) * D * BN
                              : vtloc_gh + static_cast<int64_t>(lt) * D * BN;
-    stage.load(kb, krow, kvalid, vb);
+    dma.issue(kb, !pre, p.kvs_tok, kvalid, vb, dst);
   };
 
   bf16x8 qf[C::DK];
@@ -232,14 +232,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   Flash<D> f;
   f.init();
 
-  if (ntiles > 0) {
-    load_tile(0);
-    stage.store(smem);
-  }
+  if (ntiles > 0) issue_tile(0, smem);
+  wait_tile_loads();
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) load_tile(it + 1);
+    if (it + 1 < ntiles) issue_tile(it + 1, smem + ((it + 1) & 1) * C::STAGE);
     const bool local = it >= np;
     const int pt = tr.pt0 + it;
     const int64_t key0 = local ? s_h + static_cast<int64_t>(it - np) * BN : 0;
@@ -256,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     if (!wave_active) lim = -1;
     const char* ks = smem + (it & 1) * C::STAGE;
     attend_tile<D>(ks, ks + C::KBYTES, qf, f, lim, c_log2);
-    if (it + 1 < ntiles) stage.store(smem + ((it + 1) & 1) * C::STAGE);
+    wait_tile_loads();
     __syncthreads();
   }
 

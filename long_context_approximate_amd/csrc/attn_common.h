@@ -115,6 +115,110 @@ struct TileStage {
   }
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// A generic pointer into __shared__ memory as an LDS-address-space pointer.
+__device__ inline lds_ptr_t as_lds(char* ptr) { return (lds_ptr_t)(ptr); }
+// One 16-byte-per-lane buffer load into LDS (64 lanes -> 1 KB at dst + 16 * lane).
+// A plain function, not a template member: with the builtin called directly from
+// the kernel templates, the host pass emitted the launch stub of only one of them.
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_ptr_t dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voffset, 0, 0, 0);
+}
+
+// Direct global -> LDS tile loads (buffer_load_dwordx4 with the LDS bit): no
+// register staging and no LDS store instructions. A stage (K rows of KROWB bytes,
+// then V^T rows of VROWB bytes, each row ending in a 16-byte pad) is a run of
+// 16-byte slots; one load writes 64 consecutive slots (1 KB at the wave's LDS
+// address + 16 * lane), and each lane fetches the global chunk that belongs in its
+// slot. Pad slots, and K rows past the valid count, use offsets beyond the buffer's
+// range: the hardware reads nothing for them. Wave w loads K blocks 8r + w and V^T
+// blocks 8r + w in full rounds of eight, then at most one of the leftover blocks.
+// Completion is tracked by vmcnt: wait_tile_loads() then a barrier publishes a stage.
+template <int D>
+struct TileDma {
+  using C = Cfg<D>;
+  static constexpr int KSPR = C::KROWB / 16, VSPR = VROWB / 16;   // slots per row
+  static constexpr int KBLK = C::KBYTES / 1024, VBLK = C::VBYTES / 1024;
+  static constexpr int KR = KBLK / kWaves, VR = VBLK / kWaves;     // full rounds
+  static constexpr int KREM = KBLK % kWaves, VREM = VBLK % kWaves;
+  static_assert(C::KBYTES % 1024 == 0 && C::VBYTES % 1024 == 0, "stage must be whole 1 KB blocks");
+  static_assert(KREM + VREM <= kWaves, "leftover blocks must fit one round");
+  static constexpr uint32_t kOut = 0x7FFFFFF0u;   // past every buffer range
+  static constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
+  int wave;                            // this wave's index (wave-uniform)
+  uint32_t kpre[KR], kloc[KR];         // byte offsets of K rows: 2D-byte rows, runtime stride
+  uint32_t voff[VR];                   // byte offsets into the V^T tile
+  uint32_t tpre, tloc;                 // the leftover block's offsets (V^T: both equal)
+  int tkind;                           // leftover block: 0 K, 1 V^T, 2 none (wave-uniform)
+  int tlds;                            // its LDS offset inside a stage
+
+  __device__ static void k_offsets(int blk, int lane, int64_t krow_loc, uint32_t& pre,
+                                   uint32_t& loc) {
+    const int sl = blk * 64 + lane, r = sl / KSPR, c = sl % KSPR;
+    pre = kOut;
+    loc = kOut;
+    if (c < D / 8) {
+      pre = static_cast<uint32_t>(r * (2 * D) + c * 16);
+      loc = static_cast<uint32_t>(r * krow_loc * 2 + c * 16);
+    }
+  }
+  __device__ static uint32_t v_offset(int blk, int lane) {
+    const int sl = blk * 64 + lane, r = sl / VSPR, c = sl % VSPR;
+    return c < BN / 8 ? static_cast<uint32_t>(r * (2 * BN) + c * 16) : kOut;
+  }
+
+  // krow_loc: row stride (elements) of K read in place; (BN - 1) * krow_loc * 2 + 2D
+  // must stay below 2^31 (the plan checks this).
+  __device__ void init(int64_t krow_loc) {
+    wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < KR; ++r) k_offsets(r * kWaves + wave, lane, krow_loc, kpre[r], kloc[r]);
+#pragma unroll
+    for (int r = 0; r < VR; ++r) voff[r] = v_offset(r * kWaves + wave, lane);
+    tkind = wave < KREM ? 0 : (wave < KREM + VREM ? 1 : 2);
+    tpre = kOut;
+    tloc = kOut;
+    tlds = 0;
+    if (tkind == 0) {
+      k_offsets(KR * kWaves + wave, lane, krow_loc, tpre, tloc);
+      tlds = (KR * kWaves + wave) * 1024;
+    } else if (tkind == 1) {
+      tpre = tloc = v_offset(VR * kWaves + wave - KREM, lane);
+      tlds = C::KBYTES + (VR * kWaves + wave - KREM) * 1024;
+    }
+  }
+  // kb: first K row of the tile; local: rows use the runtime stride krow (else 2D
+  // bytes per row); kvalid: K rows present (>= 1); vb: the V^T tile [D][BN].
+  __device__ void issue(const uint16_t* kb, bool local, int64_t krow, int64_t kvalid,
+                        const uint16_t* vb, char* dst) const {
+    const int64_t rows = kvalid < BN ? kvalid : BN;
+    const int64_t stride = local ? krow : D;
+    const int kbytes = static_cast<int>((rows - 1) * stride * 2 + 2 * D);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kb), static_cast<short>(0), kbytes, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vb), static_cast<short>(0), D * BN * 2, kRsrcFlags);
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const uint32_t a = kpre[r], b = kloc[r];
+      load_lds16(rk, as_lds(dst + (r * kWaves + wave) * 1024), local ? b : a);
+    }
+#pragma unroll
+    for (int r = 0; r < VR; ++r)
+      load_lds16(rv, as_lds(dst + C::KBYTES + (r * kWaves + wave) * 1024), voff[r]);
+    const uint32_t ta = tpre, tb = tloc;
+    if (tkind == 0)
+      load_lds16(rk, as_lds(dst + tlds), local ? tb : ta);
+    else if (tkind == 1)
+      load_lds16(rv, as_lds(dst + tlds), ta);
+  }
+};
+
+// Wait for this wave's outstanding global -> LDS tile loads (vmcnt(0); other
+// counters left alone). A barrier after it makes the stage visible to every wave.
+__device__ inline void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Per-wave flash state for 32 queries: O^T accumulators, running reference max
 // (log2 units) and this lane's partial row sum (keys it holds; the partner lane
 // l ^ 32 holds the rest of the query's keys).

@@ -61,6 +61,9 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
     if (st < 0) return SPAVA_ERR_SHAPE;
     if (st % unit != 0) return SPAVA_ERR_ALIGN;
   }
+  // The attention reads K tiles in place through 32-bit buffer offsets: 63 token rows
+  // of stride plus one row of 2 * head_dim bytes must stay below 2^31.
+  if (s->kv_stride_tok > (INT32_MAX - 2 * 128) / (2 * (kKeyTile - 1))) return SPAVA_ERR_SHAPE;
   p->N = s->seq_len;
   p->H = s->num_hosts;
   p->Hq = s->num_q_heads;
