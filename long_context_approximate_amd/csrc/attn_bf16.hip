@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   const int ntiles = np + nloc;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t qw0 = q0 + static_cast<int64_t>(kWaveQ) * w;   // first query of this wave
   const bool wave_active = qw0 < e_h;
@@ -232,28 +232,41 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   Flash<D> f;
   f.init();
 
+  // Which tiles need a mask, decided once per wave so the tile loop only compares
+  // indices: local tiles from it_diag on touch this wave's causal diagonal
+  // (key0 + BN - 1 > qw0, i.e. (it - np) * BN > qw0 - s_h - BN + 1); the last prefix
+  // tile (it_edge) is partial when the prefix length is not a multiple of BN; a wave
+  // past the block end masks everything.
+  const int64_t rel0 = qw0 - s_h;
+  const int first_diag = rel0 >= BN - 1 ? static_cast<int>((rel0 - (BN - 1)) / BN) + 1 : 0;
+  const int it_diag = tr.local ? np + first_diag : ntiles;
+  const int it_edge =
+      ((L % BN) != 0 && npre - 1 >= tr.pt0 && npre - 1 < tr.pt1) ? npre - 1 - tr.pt0 : -1;
+  const int qrel = static_cast<int>(qi - s_h);   // this lane's query inside the block
+
   if (ntiles > 0) issue_tile(0, smem);
   wait_tile_loads();
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) issue_tile(it + 1, smem + ((it + 1) & 1) * C::STAGE);
-    const bool local = it >= np;
-    const int pt = tr.pt0 + it;
-    const int64_t key0 = local ? s_h + static_cast<int64_t>(it - np) * BN : 0;
-    // Last visible key of the tile: the prefix length in the last prefix tile, the
-    // causal diagonal in a local tile. Tiles past this wave's queries are processed
-    // fully masked (lim = -1) rather than branched around, which keeps the O
-    // accumulators in place across iterations.
+    // Last visible key of a masked tile: the prefix length in the partial prefix
+    // tile, the causal diagonal in a local tile. Tiles past this wave's queries are
+    // processed fully masked (lim = -1) rather than branched around, which keeps the
+    // O accumulators in place across iterations.
+    const bool diag = it >= it_diag;
+    const bool masked = diag || it == it_edge || !wave_active;
     int lim = BN - 1;
-    if (!local && pt == npre - 1 && (L % BN) != 0) lim = L - pt * BN - 1;
-    if (local && key0 + BN - 1 > qw0) {
-      const int64_t rel = qi - key0;               // integer select (no floating max)
-      lim = rel < 0 ? -1 : static_cast<int>(rel);
+    if (masked) {
+      if (it == it_edge) lim = L - (tr.pt0 + it) * BN - 1;
+      if (diag) {
+        const int rel = qrel - (it - np) * BN;      // integer select (no floating max)
+        lim = rel < 0 ? -1 : rel;
+      }
+      if (!wave_active) lim = -1;
     }
-    if (!wave_active) lim = -1;
     const char* ks = smem + (it & 1) * C::STAGE;
-    attend_tile<D>(ks, ks + C::KBYTES, qf, f, lim, c_log2);
+    attend_tile<D>(ks, ks + C::KBYTES, qf, f, masked, lim, c_log2);
     wait_tile_loads();
     __syncthreads();
   }

@@ -269,14 +269,15 @@ __device__ inline float exp_tile(const f32x16 (&s)[2], float ref, float c_log2, 
   return sum0 + sum1;
 }
 
-// One 64-key tile for this wave's 32 queries: S^T = K Q^T, hide keys kk > lim (kk =
-// key index inside the tile; lim >= 63 means no mask), online softmax in the log2
-// domain against the running reference, then O^T += V^T P^T. LDS fragments are read
-// in batches ahead of their products (all K fragments first; V^T fragments in two
-// halves), so each batch is in flight while earlier work runs.
+// One 64-key tile for this wave's 32 queries: S^T = K Q^T, then, when `masked` (a
+// wave-uniform flag), hide keys kk > lim (kk = key index inside the tile; lim >= 63
+// hides nothing), online softmax in the log2 domain against the running reference,
+// then O^T += V^T P^T. LDS fragments are read in batches ahead of their products (all
+// K fragments first; V^T fragments in two halves), so each batch is in flight while
+// earlier work runs.
 template <int D>
 __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 (&qf)[Cfg<D>::DK],
-                                   Flash<D>& f, int lim, float c_log2) {
+                                   Flash<D>& f, bool masked, int lim, float c_log2) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
@@ -310,7 +311,7 @@ __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 
   read_v(0);
   read_v(1);
   __builtin_amdgcn_sched_barrier(0);
-  if (lim < BN - 1) {
+  if (masked && lim < BN - 1) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
