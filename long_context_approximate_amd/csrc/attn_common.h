@@ -311,7 +311,7 @@ __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 
   read_v(0);
   read_v(1);
   __builtin_amdgcn_sched_barrier(0);
-  if (masked && lim < BN - 1) {
+  if (masked) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

@@ -98,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
       int64_t lim = nkeys - key0 - 1;
       if (self && qi - key0 < lim) lim = qi - key0;
       const char* ks = smem + (it & 1) * C::STAGE;
-      attend_tile<D>(ks, ks + C::KBYTES, qf, f, true, lim < BN - 1 ? static_cast<int>(lim) : BN - 1,
-                     c_log2);
+      const int lim32 = lim < BN - 1 ? static_cast<int>(lim) : BN - 1;
+      attend_tile<D>(ks, ks + C::KBYTES, qf, f, __any(lim32 < BN - 1) != 0, lim32, c_log2);
     }
     if (it + 1 < ntiles) stage.store(smem + ((it + 1) & 1) * C::STAGE);
     __syncthreads();
