@@ -215,16 +215,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   // place and V^T from the block's transposed tiles.
   TileDma<D> dma;
   dma.init(p.kvs_tok);
+  // Per-workgroup tile bases and K ranges, so issuing a tile is a few scalar adds:
+  // full local tiles share one range; only a block's last tile can be partial.
+  const uint16_t* kpre0 = kpre_g + static_cast<int64_t>(tr.pt0) * BN * D;
+  const uint16_t* vpre0 = vtpre_g + static_cast<int64_t>(tr.pt0) * D * BN;
+  const uint16_t* kloc0 = k_g + s_h * p.kvs_tok;
+  const int64_t kloc_step = static_cast<int64_t>(BN) * p.kvs_tok;
+  const int kbytes_pre = TileDma<D>::k_range(BN, D);
+  const int kbytes_loc = TileDma<D>::k_range(BN, p.kvs_tok);
+  const int lt_part = (p.nb % BN) != 0 ? p.nb / BN : -1;     // partial local tile
+  const int kbytes_part = TileDma<D>::k_range(p.nb % BN, p.kvs_tok);
   auto issue_tile = [&](int it, char* dst) {
-    const bool pre = it < np;
-    const int pt = tr.pt0 + it;
-    const int lt = it - np;
-    const int64_t key0 = s_h + static_cast<int64_t>(lt) * BN;
-    const uint16_t* kb = pre ? kpre_g + static_cast<int64_t>(pt) * BN * D : k_g + key0 * p.kvs_tok;
-    const int64_t kvalid = pre ? BN : e_h - key0;
-    const uint16_t* vb = pre ? vtpre_g + static_cast<int64_t>(pt) * D * BN
-                             : vtloc_gh + static_cast<int64_t>(lt) * D * BN;
-    dma.issue(kb, !pre, p.kvs_tok, kvalid, vb, dst);
+    if (it < np) {
+      dma.issue(kpre0 + static_cast<int64_t>(it) * BN * D, false, kbytes_pre,
+                vpre0 + static_cast<int64_t>(it) * D * BN, dst);
+    } else {
+      const int lt = it - np;
+      dma.issue(kloc0 + lt * kloc_step, true, lt == lt_part ? kbytes_part : kbytes_loc,
+                vtloc_gh + static_cast<int64_t>(lt) * D * BN, dst);
+    }
   };
 
   bf16x8 qf[C::DK];

@@ -188,13 +188,15 @@ struct TileDma {
       tlds = C::KBYTES + (VR * kWaves + wave - KREM) * 1024;
     }
   }
-  // kb: first K row of the tile; local: rows use the runtime stride krow (else 2D
-  // bytes per row); kvalid: K rows present (>= 1); vb: the V^T tile [D][BN].
-  __device__ void issue(const uint16_t* kb, bool local, int64_t krow, int64_t kvalid,
-                        const uint16_t* vb, char* dst) const {
-    const int64_t rows = kvalid < BN ? kvalid : BN;
-    const int64_t stride = local ? krow : D;
-    const int kbytes = static_cast<int>((rows - 1) * stride * 2 + 2 * D);
+  // Bytes of a K tile's buffer range: `rows` rows of `stride` elements, the last one
+  // ending after its 2D bytes of data.
+  __device__ static int k_range(int64_t rows, int64_t stride) {
+    return static_cast<int>((rows - 1) * stride * 2 + 2 * D);
+  }
+  // kb: first K row of the tile; local: rows use the runtime stride (else 2D bytes
+  // per row); kbytes: k_range of the rows present; vb: the V^T tile [D][BN].
+  __device__ void issue(const uint16_t* kb, bool local, int kbytes, const uint16_t* vb,
+                        char* dst) const {
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kb), static_cast<short>(0), kbytes, kRsrcFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
