@@ -64,6 +64,9 @@ def _shape(**kw):
     ({"dtype": 9}, ERR_DTYPE),
     ({"sm_scale": float("nan")}, ERR_SHAPE),
     ({"strides": (1028, 128, 256, 128, 1024, 128)}, ERR_ALIGN),
+    # K rows are read through 32-bit buffer offsets: 63 token strides + one row < 2^31 B
+    ({"strides": (1024, 128, 17043512, 128, 1024, 128)}, OK),
+    ({"strides": (1024, 128, 17043520, 128, 1024, 128)}, ERR_SHAPE),
     ({"num_hosts": 1, "anchor_len": 0}, OK),
     ({"anchor_len": 1024, "passing_len": 0}, OK),
 ])
