@@ -46,9 +46,6 @@ struct Cfg {
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int DK = D / 16;           // MFMA steps over the head dim
   static constexpr int DM = D / 32;           // 32-row blocks of O^T
-  static constexpr int KCH = BN * D / 8 / kThreads;   // 16-byte K chunks per thread per tile
-  static constexpr int VCH = D * BN / 8 / kThreads;   // 16-byte V^T chunks per thread per tile
-  static_assert(KCH >= 1 && VCH >= 1, "tile too small for the workgroup");
 };
 
 // Key offset inside a 16-key chunk for MFMA reduction slot s (an involution).
@@ -77,43 +74,6 @@ __device__ inline void store_vt_tile(const uint16_t (*Vs)[D + 8], uint16_t* dst)
     *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(d) * BN + sc * 8) = pk;
   }
 }
-
-// Global -> register staging of one tile (K rows and a V^T tile) and the register ->
-// LDS store, for a workgroup of kThreads threads. `kb`/`krow`/`kvalid` describe the K
-// rows (element pointer, row stride, rows present); rows past kvalid are zero.
-template <int D>
-struct TileStage {
-  u32x4 kreg[Cfg<D>::KCH], vreg[Cfg<D>::VCH];
-  __device__ void load(const uint16_t* kb, int64_t krow, int64_t kvalid, const uint16_t* vb) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < Cfg<D>::KCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 8), col = c % (D / 8);
-      kreg[i] = row < kvalid ? *reinterpret_cast<const u32x4*>(kb + row * krow + col * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg<D>::VCH; ++i)
-      vreg[i] = *reinterpret_cast<const u32x4*>(vb + (tid + kThreads * i) * 8);
-  }
-  __device__ void store(char* ks) const {
-    const int tid = threadIdx.x;
-    char* vs = ks + Cfg<D>::KBYTES;
-#pragma unroll
-    for (int i = 0; i < Cfg<D>::KCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + row * Cfg<D>::KROWB + col * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg<D>::VCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int d = c / (BN / 8), col = c % (BN / 8);
-      *reinterpret_cast<u32x4*>(vs + d * VROWB + col * 16) = vreg[i];
-    }
-  }
-};
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // A generic pointer into __shared__ memory as an LDS-address-space pointer.

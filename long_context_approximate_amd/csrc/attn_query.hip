@@ -75,10 +75,13 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
   const uint16_t* vtbase = self ? vtq + static_cast<int64_t>(g) * qkt * D * BN
                                 : vtctx + (static_cast<int64_t>(g) * p.H + ph) * p.loc_tiles * D * BN;
 
-  TileStage<D> stage;
-  auto load_tile = [&](int it) {
+  TileDma<D> dma;
+  dma.init(p.kvs_tok);
+  auto issue_tile = [&](int it, char* dst) {
     const int64_t key0 = static_cast<int64_t>(it) * BN;
-    stage.load(kbase + key0 * p.kvs_tok, p.kvs_tok, nkeys - key0, vtbase + it * D * BN);
+    const int64_t rows = nkeys - key0 < BN ? nkeys - key0 : BN;
+    dma.issue(kbase + key0 * p.kvs_tok, true, TileDma<D>::k_range(rows, p.kvs_tok),
+              vtbase + static_cast<int64_t>(it) * D * BN, dst);
   };
 
   bf16x8 qf[C::DK];
@@ -86,11 +89,11 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
   Flash<D> f;
   f.init();
 
-  load_tile(0);
-  stage.store(smem);
+  if (ntiles > 0) issue_tile(0, smem);
+  wait_tile_loads();
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) load_tile(it + 1);
+    if (it + 1 < ntiles) issue_tile(it + 1, smem + ((it + 1) & 1) * C::STAGE);
     const int64_t key0 = static_cast<int64_t>(it) * BN;
     const bool skip = !wave_active || (self && key0 > qw_last);
     if (!skip) {
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
       const int lim32 = lim < BN - 1 ? static_cast<int>(lim) : BN - 1;
       attend_tile<D>(ks, ks + C::KBYTES, qf, f, __any(lim32 < BN - 1) != 0, lim32, c_log2);
     }
-    if (it + 1 < ntiles) stage.store(smem + ((it + 1) & 1) * C::STAGE);
+    wait_tile_loads();
     __syncthreads();
   }
   const float ltot = flash_rowsum<D>(f);
