@@ -57,28 +57,37 @@ def attn_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def clock_from_profile():
-    """Average shader clock (GHz) during the attention kernel from the committed
-    GRBM_GUI_ACTIVE counter run, or None when missing or stale."""
+def _profile_field(*keys):
+    """A number from the committed rocprofv3 counter summary, or None when the summary
+    is missing, lacks the field, or the attention source changed since it was taken."""
     try:
         rec = json.load(open(PMC_SUMMARY))
         if rec.get("attn_sources_sha256") != attn_sources_sha256():
             return None
-        return float(rec["attn_clock_ghz"])
-    except (OSError, ValueError, KeyError):
+        for k in keys:
+            rec = rec[k]
+        return float(rec)
+    except (OSError, ValueError, KeyError, TypeError):
         return None
+
+
+def clock_from_profile():
+    """Average shader clock (GHz) during the attention kernel (GRBM_GUI_ACTIVE run)."""
+    return _profile_field("attn_clock_ghz")
 
 
 def traffic_from_profile():
-    """HBM bytes per attention launch from the committed rocprofv3 PMC summary, or None
-    when the summary is missing or the kernel source changed since it was taken."""
-    try:
-        rec = json.load(open(PMC_SUMMARY))
-        if rec.get("attn_sources_sha256") != attn_sources_sha256():
-            return None
-        return float(rec["hbm_bytes_per_launch"])
-    except (OSError, ValueError, KeyError):
-        return None
+    """HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE runs, calibrated)."""
+    return _profile_field("hbm_bytes_per_launch")
+
+
+def score_flops(cfg) -> float:
+    """fp64 FLOP of the window-score dot products: 2 d per (observer row, visible key);
+    row i of the last w of a block sees the block's keys up to i."""
+    H, hkv, G = cfg.num_hosts, cfg.num_kv_heads, cfg.num_q_heads // cfg.num_kv_heads
+    nb, w = cfg.seq_len // H, cfg.window
+    visits = w * nb - w * (w - 1) // 2
+    return 2.0 * cfg.head_dim * max(H - 1, 0) * hkv * G * visits
 
 
 def cpu_baseline(cfg, x, budget_rows=16384, pairs_sampled=8):
@@ -330,12 +339,25 @@ def main():
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_from_profile()},
     }
+    rec["score_fp64_gflops"] = score_flops(cfg) / t_sel / 1e9
     clock = clock_from_profile()
     if clock is not None:
         # The published peak assumes 2.4 GHz; under sustained matrix load the chip runs
         # slower, so also report against the peak at the measured clock.
         adj = PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ
         rec["clock_adjusted"] = {"clock_ghz": clock, "peak": adj, "frac": tflops / adj}
+    # From the committed counter runs of this attention source (None when stale):
+    # matrix-core busy fraction and HBM rate of the attention kernel, and the gather
+    # (prep) kernel's duration.
+    busy = _profile_field("attn_mfma_busy_frac")
+    dur = _profile_field("attn_kernel", "dur_us")
+    hbm = traffic_from_profile()
+    rec["profiled"] = {
+        "attn_mfma_busy_frac": busy,
+        "attn_hbm_gb_per_s": hbm / dur / 1e3 if hbm is not None and dur else None,
+        "t_gather_ms": (lambda v: v / 1e3 if v is not None else None)(
+            _profile_field("prep_kernel", "dur_us")),
+    }
     if not args.no_extras:
         rec["schedules_attn_ms"] = time_schedules(shape, q, k, v, idx, out, lse, ws_attn, stream)
         rec["dense_causal"] = dense_baseline(cfg, q, k, v, stream, t_step)

@@ -62,3 +62,23 @@ def test_gpus_above_one_exit_with_a_message(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def _brute_force_score_visits(cfg):
+    """Visible (observer row, key) pairs of the window scores, counted one by one: row i
+    of the last w queries of block j >= 1 sees the block's keys up to i."""
+    H, nb, w = cfg.num_hosts, cfg.block_len, cfg.window
+    per_head = sum(i - j * nb + 1 for j in range(1, H) for i in range((j + 1) * nb - w, (j + 1) * nb))
+    return per_head * cfg.num_q_heads   # G rows per KV head and Hkv KV heads = Hq rows
+
+
+@pytest.mark.parametrize("cfg", [small_config(), CONFIGS["tiny_f32_512"], CONFIGS["h4_16k"]],
+                         ids=lambda c: c.name)
+def test_score_flops_match_brute_force(cfg):
+    assert bench.score_flops(cfg) == 2 * cfg.head_dim * _brute_force_score_visits(cfg)
+
+
+def test_score_flops_of_the_named_workloads():
+    # 2 d (H-1) Hkv G (w n_b - w(w-1)/2), worked by hand for 128K:
+    # 2*128 * 7*4*7 * (128*16384 - 8128) = 50,176 * 2,089,024 = 104,818,868,224
+    assert bench.score_flops(CONFIGS["h8_128k"]) == 104_818_868_224
