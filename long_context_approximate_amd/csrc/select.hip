@@ -163,7 +163,8 @@ __device__ inline void load_keys(const Plan& p, const T* k, int g, int64_t key0,
 // logit minus a running or final row maximum, so it is never positive. Tang's
 // table-driven method: y = (64 n + j) ln2/64 + r with |r| <= ln2/128, so
 // exp(y) = 2^n * 2^(j/64) * exp(r); 2^(j/64) comes from a 64-entry table in LDS and
-// exp(r) from its degree-5 Taylor polynomial (truncation error below 2^-60). ln2/64 is
+// exp(r) from its degree-5 Taylor polynomial (truncation error below 2^-54, a sixth of
+// an ulp of 1). ln2/64 is
 // split into a 36-bit head (exact products k * head for |k| < 2^17) and a tail.
 // Arguments below -745.2 underflow to 0.
 constexpr int kExpTab = 64;
