@@ -173,6 +173,30 @@ def test_strided_layout():
     _check_full(cfg, got, ref)
 
 
+def test_large_kv_token_stride():
+    # k/v rows 64K elements (128 KB) apart: the tile loads address K rows in place through
+    # 32-bit buffer offsets of up to 63 token strides, and clip the ragged last tile.
+    torch = _torch()
+    cfg = small_config(name="wide_kv", seq_len=1200, num_hosts=2, seed=27)
+    n, hq, hkv, d = cfg.seq_len, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    slots = 65536 // d
+
+    def make(dev):
+        kw = torch.zeros((n, slots, d), dtype=torch.bfloat16, device="cuda")
+        vw = torch.zeros((n, slots, d), dtype=torch.bfloat16, device="cuda")
+        kw[:, :hkv] = dev["k"]
+        vw[:, :hkv] = dev["v"]
+        return {"q": dev["q"], "k": kw, "v": vw}
+
+    strides = {"shape": (hq * d, d, slots * d, d, hq * d, d), "make": make,
+               "out": lambda: torch.full((n, hq, d), float("nan"), dtype=torch.bfloat16,
+                                         device="cuda")}
+    got, x = _gpu_run(cfg, strides=strides)
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    _check_selection(cfg, got, ref)
+    _check_full(cfg, got, ref)
+
+
 def test_deterministic_bitwise():
     cfg = small_config(name="det", seq_len=3072, num_hosts=4, seed=25)
     x = make_inputs(cfg)
