@@ -133,7 +133,7 @@ __device__ inline int pair_cost(const Plan& p, int pair, int mode) {
 // paired as (p, H-1-p), the pages' host pairing, tiles of a pair alternating.
 __global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restrict__ order,
                                                        int mode) {
-  __shared__ int cost[256];
+  __shared__ __attribute__((aligned(16))) int cost[256];
   const int P = p.H * p.T;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const bool valid = i < P;
@@ -147,17 +147,23 @@ __global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restri
     rank = (h == mirror) ? pr * 2 * p.T + t : pr * 2 * p.T + 2 * t + (h > mirror ? 1 : 0);
   } else {
     // Rank = number of pairs that come first (higher cost, or equal cost and lower
-    // index); the costs of each chunk of 256 pairs are computed once into LDS.
+    // index); the costs of each chunk of 256 pairs are computed once into LDS (slots
+    // past P hold -1, which never counts: costs are >= 0) and read 4 at a time.
     const int ci = valid ? pair_cost(p, i, mode) : 0;
     for (int j0 = 0; j0 < P; j0 += 256) {
       __syncthreads();
-      if (j0 + static_cast<int>(threadIdx.x) < P)
-        cost[threadIdx.x] = pair_cost(p, j0 + threadIdx.x, mode);
+      const int jt = j0 + static_cast<int>(threadIdx.x);
+      cost[threadIdx.x] = jt < P ? pair_cost(p, jt, mode) : -1;
       __syncthreads();
-      const int n = min(256, P - j0);
-      for (int jj = 0; jj < n; ++jj) {
-        const int cj = cost[jj];
-        rank += (cj > ci) || (cj == ci && j0 + jj < i);
+      const int4* c4 = reinterpret_cast<const int4*>(cost);
+#pragma unroll 8
+      for (int q4 = 0; q4 < 64; ++q4) {
+        const int4 c = c4[q4];
+        const int jb = j0 + 4 * q4;
+        rank += (c.x > ci) || (c.x == ci && jb < i);
+        rank += (c.y > ci) || (c.y == ci && jb + 1 < i);
+        rank += (c.z > ci) || (c.z == ci && jb + 2 < i);
+        rank += (c.w > ci) || (c.w == ci && jb + 3 < i);
       }
     }
   }
