@@ -529,24 +529,53 @@ __global__ __launch_bounds__(1024) void topl_kernel(Plan p, const double* __rest
     const int shift = 56 - 8 * pass;
     for (int b = tid; b < 256; b += blockDim.x) hist[b] = 0;
     __syncthreads();
-    for (int t = tid; t < n; t += blockDim.x) {
-      const unsigned long long x = u[t];
-      if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 0xFF], 1u);
+    for (int base = 0; base < n; base += blockDim.x) {
+      const int t = base + tid;
+      const unsigned long long x = t < n ? u[t] : 0ull;
+      const bool m = t < n && (x & mask) == prefix;
+      const unsigned dg = static_cast<unsigned>(x >> shift) & 0xFFu;
+      // Scores share their leading bytes, so a wave's matching lanes usually carry one
+      // digit: then a single atomic adds them all.
+      const unsigned long long act = __ballot(m);
+      if (act != 0ull) {
+        const int first = __ffsll(static_cast<long long>(act)) - 1;
+        const unsigned d0 = static_cast<unsigned>(__shfl(static_cast<int>(dg), first));
+        if (__ballot(m && dg != d0) == 0ull) {
+          if (lane == first) atomicAdd(&hist[d0], static_cast<unsigned>(__popcll(act)));
+        } else if (m) {
+          atomicAdd(&hist[dg], 1u);
+        }
+      }
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0;
-      int digit = 0;
-      for (int d = 255; d >= 0; --d) {
-        const int c = static_cast<int>(hist[d]);
-        if (cum + c >= krem) {
-          digit = d;
-          break;
-        }
-        cum += c;
+    if (wave == 0) {
+      // Digits in descending order, four per lane (lane L: 255 - 4L down to 252 - 4L);
+      // a prefix sum over the lanes finds where the count from the top reaches krem.
+      unsigned c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
+      const int lsum = static_cast<int>(c[0] + c[1] + c[2] + c[3]);
+      int incl = lsum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
       }
-      s_prefix = prefix | (static_cast<unsigned long long>(digit) << shift);
-      s_k = krem - cum;
+      const unsigned long long hit = __ballot(incl >= krem);
+      if (lane == __ffsll(static_cast<long long>(hit)) - 1) {
+        int cum = incl - lsum;
+        int digit = 255 - 4 * lane - 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (cum + static_cast<int>(c[i]) >= krem) {
+            digit = 255 - 4 * lane - i;
+            break;
+          }
+          cum += static_cast<int>(c[i]);
+        }
+        s_prefix = prefix | (static_cast<unsigned long long>(digit) << shift);
+        s_k = krem - cum;
+      }
     }
     __syncthreads();
     prefix = s_prefix;
