@@ -45,18 +45,26 @@ __global__ __launch_bounds__(256) void vt_rows_kernel(const uint16_t* __restrict
                                  D * BN);
 }
 
-// grid ((H + 1) * qtiles, Hq), kThreads threads. Partial ph < H: context block ph,
-// every key visible. Partial H: the query block's own keys, causal.
+// One workgroup per (partial, query tile, query head); kThreads threads. Partial
+// ph < H: context block ph, every key visible. Partial H: the query block's own keys,
+// causal. NG = (H + 1) * qtiles * Hkv groups of G workgroups; the grid is
+// round_up(NG, 8) * G workgroups, mapped like the main attention so the G heads of one
+// KV group run on one XCD and read each K/V tile through its L2 once.
 template <int D>
 __global__ __launch_bounds__(kThreads) void query_partial_kernel(
-    Plan p, int64_t nq, int qtiles, const uint16_t* __restrict__ q_qr,
+    Plan p, int64_t nq, int qtiles, int NG, const uint16_t* __restrict__ q_qr,
     const uint16_t* __restrict__ k_qr, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vtctx, const uint16_t* __restrict__ vtq,
     float* __restrict__ part_o, float* __restrict__ part_lse, float c_log2) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
-  const int ph = blockIdx.x / qtiles, qt = blockIdx.x % qtiles;
-  const int hq = blockIdx.y, g = hq / p.G;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int gs = (slot / p.G) * 8 + xcd;
+  if (gs >= NG) return;
+  const int hl = slot % p.G;
+  const int g = gs % p.Hkv, hq = g * p.G + hl;
+  const int ph = (gs / p.Hkv) / qtiles, qt = (gs / p.Hkv) % qtiles;
   const bool self = ph == p.H;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -255,9 +263,10 @@ hipError_t launch_query_bf16(const Plan& p, int64_t nq, const uint16_t* q_qr, co
                      v_qr, nq, 1, qkt, p.kvs_tok, p.kvs_head, vtq);
   const int qtiles = static_cast<int>(cdiv(nq, kQTile));
   const float c_log2 = static_cast<float>(p.scale * 1.4426950408889634);
-  hipLaunchKernelGGL(query_partial_kernel<D>, dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq),
-                     dim3(kThreads), 0, st, p, nq, qtiles, q_qr, k_qr, k, vtctx, vtq, part_o,
-                     part_lse, c_log2);
+  const int NG = (p.H + 1) * qtiles * p.Hkv;
+  const int64_t groups = round_up(NG, 8) * p.G;
+  hipLaunchKernelGGL(query_partial_kernel<D>, dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0,
+                     st, p, nq, qtiles, NG, q_qr, k_qr, k, vtctx, vtq, part_o, part_lse, c_log2);
   const int64_t threads = nq * p.Hq * (p.D / 4);
   hipLaunchKernelGGL(query_merge_kernel<uint16_t>, dim3(static_cast<unsigned>(cdiv(threads, 256))),
                      dim3(256), 0, st, p, nq, part_o, part_lse, out, lse);

@@ -327,7 +327,9 @@ spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, cons
 // The query block's launches: 1 <= n_query <= 2^30, partial and merge grids in range.
 static bool query_launches_fit(const Plan& p, int64_t nq) {
   if (nq < 1 || nq > (int64_t(1) << 30)) return false;
-  return fits_launch({static_cast<int64_t>(p.H) + 1, cdiv(nq, kQTile), 512}) &&
+  return fits_launch({static_cast<int64_t>(p.H) + 1, cdiv(nq, kQTile), p.Hkv}) &&
+         fits_launch({round_up((static_cast<int64_t>(p.H) + 1) * cdiv(nq, kQTile) * p.Hkv, 8),
+                      p.G, 512}) &&
          fits_launch({nq, p.Hq, p.D / 4}) && fits_launch({cdiv(nq, kKeyTile), 256});
 }
 
