@@ -173,6 +173,31 @@ def test_strided_layout():
     _check_full(cfg, got, ref)
 
 
+def _random_config(seed):
+    """A seeded random small shape: hosts, ragged block length, GQA group, head dim,
+    anchor, passing length, window, dtype and key distribution all drawn."""
+    import random
+    r = random.Random(5000 + seed)
+    H = r.randint(1, 6)
+    nb = r.randint(65, min(1100, 3500 // H))
+    hkv = r.choice([1, 2, 3])
+    G = r.choice([1, 2, 4, 7]) if hkv < 3 else r.choice([1, 2])
+    return small_config(name=f"rand{seed}", seq_len=H * nb, num_hosts=H, num_q_heads=hkv * G,
+                        num_kv_heads=hkv, head_dim=r.choice([64, 128]),
+                        anchor_len=r.randint(0, nb), passing_len=r.randint(0, nb + 50),
+                        window=r.randint(1, nb), dtype=r.choice(["bf16", "bf16", "bf16", "f32"]),
+                        dist=r.choice(["normal", "student_t3"]), seed=6000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_shapes(seed):
+    cfg = _random_config(seed)
+    got, x = _gpu_run(cfg)
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    _check_selection(cfg, got, ref)
+    _check_full(cfg, got, ref)
+
+
 def test_large_kv_token_stride():
     # k/v rows 64K elements (128 KB) apart: the tile loads address K rows in place through
     # 32-bit buffer offsets of up to 63 token strides, and clip the ragged last tile.
