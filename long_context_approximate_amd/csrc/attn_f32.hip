@@ -3,7 +3,8 @@
 // Same visible set as the bf16 path (explainer "APB-V: ...", Methodik >
 // Approximativer Attention-Mechanismus > Berechnung): anchor + passing rows of the
 // earlier blocks, then the block's own causal keys. Every product, exponential and
-// sum is float32. One thread owns one query row; a workgroup of 64 threads covers 64
+// sum is float32 except the softmax denominator, which is summed in float64. One
+// thread owns one query row; a workgroup of 64 threads covers 64
 // consecutive queries of one head and streams 64-key K/V tiles through LDS.
 #include "spava_internal.h"
 
@@ -85,7 +86,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float* __res
     qr[d] = valid ? q[qi * p.qs_tok + hq * p.qs_head + d] : 0.f;
     acc[d] = 0.f;
   }
-  float m = -INFINITY, l = 0.f;
+  // The denominator is summed in float64: in float32, weights below half an ulp of the
+  // running sum would be dropped, all in the same direction.
+  float m = -INFINITY;
+  double l = 0.0;
 
   const int L = prefix_len(p, h);
   const int npre = (L + BN - 1) / BN;
@@ -124,20 +128,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float* __res
         const float alpha = expf(m - x);   // m = -inf gives 0
 #pragma unroll
         for (int d = 0; d < D; ++d) acc[d] *= alpha;
-        l *= alpha;
+        l *= static_cast<double>(alpha);
         m = x;
       }
       const float pe = expf(x - m);
-      l += pe;
+      l += static_cast<double>(pe);
 #pragma unroll
       for (int d = 0; d < D; ++d) acc[d] = fmaf(pe, Vs[kk][d], acc[d]);
     }
   }
   if (!valid) return;
-  const float inv = 1.f / l;
+  const float inv = static_cast<float>(1.0 / l);
 #pragma unroll
   for (int d = 0; d < D; ++d) out[qi * p.os_tok + hq * p.os_head + d] = acc[d] * inv;
-  if (lse) lse[static_cast<int64_t>(hq) * p.N + qi] = m + logf(l);
+  if (lse)
+    lse[static_cast<int64_t>(hq) * p.N + qi] = static_cast<float>(static_cast<double>(m) + log(l));
 }
 
 template <int D>

@@ -138,7 +138,7 @@ template <int D>
 __global__ __launch_bounds__(64) void query_partial_f32_kernel(
     Plan p, int64_t nq, int qtiles, const float* __restrict__ q_qr, const float* __restrict__ k_qr,
     const float* __restrict__ v_qr, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ part_o, double* __restrict__ part_lse) {
   __shared__ float Ks[BN][D + 1];
   __shared__ float Vs[BN][D + 1];
   const int ph = blockIdx.x / qtiles, qt = blockIdx.x % qtiles;
@@ -159,7 +159,10 @@ __global__ __launch_bounds__(64) void query_partial_f32_kernel(
     qr[d] = valid ? q_qr[qi * p.qs_tok + hq * p.qs_head + d] : 0.f;
     acc[d] = 0.f;
   }
-  float m = -INFINITY, l = 0.f;
+  // The denominator is summed in float64: in float32, weights below half an ulp of the
+  // running sum would be dropped, all in the same direction.
+  float m = -INFINITY;
+  double l = 0.0;
   for (int64_t key0 = 0; key0 < nkeys; key0 += BN) {
     __syncthreads();
     for (int c = tid; c < BN * D; c += 64) {
@@ -186,21 +189,24 @@ __global__ __launch_bounds__(64) void query_partial_f32_kernel(
         const float alpha = expf(m - x);
 #pragma unroll
         for (int d = 0; d < D; ++d) acc[d] *= alpha;
-        l *= alpha;
+        l *= static_cast<double>(alpha);
         m = x;
       }
       const float pe = expf(x - m);
-      l += pe;
+      l += static_cast<double>(pe);
 #pragma unroll
       for (int d = 0; d < D; ++d) acc[d] = fmaf(pe, Vs[kk][d], acc[d]);
     }
   }
   if (!valid) return;
-  const float inv = 1.f / l;
+  const float inv = static_cast<float>(1.0 / l);
   float* op = part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
-  part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] = m + logf(l);
+  // The partial's LSE is kept in float64: the merge weights exp(LSE_h - LSE) would
+  // otherwise carry the float32 rounding of LSE values of magnitude ~10-50.
+  part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] =
+      static_cast<double>(m) + log(l);
 }
 
 __device__ inline void store4(uint16_t* dst, float4 v) {
@@ -212,11 +218,12 @@ __device__ inline void store4(uint16_t* dst, float4 v) {
 }
 __device__ inline void store4(float* dst, float4 v) { *reinterpret_cast<float4*>(dst) = v; }
 
-// One thread per (row, head, 4 dims): LSE merge of the H + 1 partials.
-template <typename T>
+// One thread per (row, head, 4 dims): LSE merge of the H + 1 partials, computed in the
+// precision L of the stored partial LSEs (float for bf16 outputs, double for float32).
+template <typename T, typename L>
 __global__ __launch_bounds__(256) void query_merge_kernel(Plan p, int64_t nq,
                                                           const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse,
+                                                          const L* __restrict__ part_lse,
                                                           T* __restrict__ out, float* __restrict__ lse) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int dq = p.D / 4;
@@ -225,16 +232,17 @@ __global__ __launch_bounds__(256) void query_merge_kernel(Plan p, int64_t nq,
   const int64_t rh = t / dq;
   const int hq = static_cast<int>(rh % p.Hq);
   const int64_t qi = rh / p.Hq;
-  float m = -INFINITY;
+  L m = -INFINITY;
   for (int ph = 0; ph <= p.H; ++ph)
-    m = fmaxf(m, part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi]);
-  float ssum = 0.f;
+    m = fmax(m, part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi]);
+  L ssum = 0;
   for (int ph = 0; ph <= p.H; ++ph)
-    ssum += expf(part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] - m);
-  const float total = m + logf(ssum);
+    ssum += exp(part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] - m);
+  const L total = m + log(ssum);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int ph = 0; ph <= p.H; ++ph) {
-    const float wgt = expf(part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] - total);
+    const float wgt =
+        static_cast<float>(exp(part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] - total));
     const float4 o = *reinterpret_cast<const float4*>(
         part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * p.D + d4 * 4);
     acc.x = fmaf(wgt, o.x, acc.x);
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(256) void query_merge_kernel(Plan p, int64_t nq,
     acc.w = fmaf(wgt, o.w, acc.w);
   }
   store4(out + qi * p.os_tok + hq * p.os_head + d4 * 4, acc);
-  if (lse && d4 == 0) lse[static_cast<int64_t>(hq) * nq + qi] = total;
+  if (lse && d4 == 0) lse[static_cast<int64_t>(hq) * nq + qi] = static_cast<float>(total);
 }
 
 template <int D>
@@ -268,7 +276,7 @@ hipError_t launch_query_bf16(const Plan& p, int64_t nq, const uint16_t* q_qr, co
   hipLaunchKernelGGL(query_partial_kernel<D>, dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0,
                      st, p, nq, qtiles, NG, q_qr, k_qr, k, vtctx, vtq, part_o, part_lse, c_log2);
   const int64_t threads = nq * p.Hq * (p.D / 4);
-  hipLaunchKernelGGL(query_merge_kernel<uint16_t>, dim3(static_cast<unsigned>(cdiv(threads, 256))),
+  hipLaunchKernelGGL((query_merge_kernel<uint16_t, float>), dim3(static_cast<unsigned>(cdiv(threads, 256))),
                      dim3(256), 0, st, p, nq, part_o, part_lse, out, lse);
   return hipGetLastError();
 }
@@ -279,13 +287,13 @@ hipError_t launch_query_f32(const Plan& p, int64_t nq, const float* q_qr, const 
                             float* lse, char* ws, hipStream_t st) {
   const QueryWs w = query_ws_layout(p, nq);
   float* part_o = reinterpret_cast<float*>(ws + w.part_o);
-  float* part_lse = reinterpret_cast<float*>(ws + w.part_lse);
+  double* part_lse = reinterpret_cast<double*>(ws + w.part_lse);
   const int qtiles = static_cast<int>(cdiv(nq, BN));
   hipLaunchKernelGGL(query_partial_f32_kernel<D>,
                      dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq), dim3(64), 0, st, p, nq,
                      qtiles, q_qr, k_qr, v_qr, k, v, part_o, part_lse);
   const int64_t threads = nq * p.Hq * (p.D / 4);
-  hipLaunchKernelGGL(query_merge_kernel<float>, dim3(static_cast<unsigned>(cdiv(threads, 256))),
+  hipLaunchKernelGGL((query_merge_kernel<float, double>), dim3(static_cast<unsigned>(cdiv(threads, 256))),
                      dim3(256), 0, st, p, nq, part_o, part_lse, out, lse);
   return hipGetLastError();
 }

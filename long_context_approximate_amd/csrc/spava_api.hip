@@ -199,7 +199,8 @@ QueryWs query_ws_layout(const Plan& p, int64_t nq) {
   size_t cur = 0;
   const size_t parts = static_cast<size_t>(p.H + 1);
   w.part_o = region(cur, parts * nq * p.Hq * p.D * sizeof(float));
-  w.part_lse = region(cur, parts * p.Hq * nq * sizeof(float));
+  // float32 inputs keep the partial LSEs in float64 (the merge weights need them).
+  w.part_lse = region(cur, parts * p.Hq * nq * (p.dtype == SPAVA_BF16 ? sizeof(float) : sizeof(double)));
   const bool bf = p.dtype == SPAVA_BF16;
   w.vtctx = region(cur, bf ? static_cast<size_t>(p.Hkv) * p.H * p.loc_tiles * kKeyTile * p.D * 2 : 0);
   w.vtq = region(cur, bf ? static_cast<size_t>(p.Hkv) * cdiv(nq, kKeyTile) * kKeyTile * p.D * 2 : 0);

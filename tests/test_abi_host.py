@@ -194,6 +194,11 @@ def test_query_entry_rejects_bad_arguments_without_touching_the_gpu(lib):
     expect = (r(5 * 256 * 8 * 128 * 4) + r(5 * 8 * 256 * 4) + r(2 * 4 * 16 * 64 * 128 * 2)
               + r(2 * 4 * 64 * 128 * 2))
     assert n.value == expect
+    # float32 inputs: partial LSEs in float64, no V^T tiles.
+    sh32 = _shape(dtype=spava.SPAVA_F32)
+    assert lib.spava_query_workspace_bytes(ctypes.byref(sh32), 256, ctypes.byref(n)) == OK
+    assert n.value == r(5 * 256 * 8 * 128 * 4) + r(5 * 8 * 256 * 8)
+    assert lib.spava_query_workspace_bytes(ctypes.byref(sh), 256, ctypes.byref(n)) == OK
     f = lib.spava_query_attn_fwd
     s = ctypes.byref(sh)
     assert f(s, 256, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value, None) == ERR_NULL

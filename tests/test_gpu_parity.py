@@ -572,3 +572,51 @@ def test_query_aware_ties_go_to_lower_positions():
         cand = oracle.passing_candidates(sh, j)
         for g in range(cfg.num_kv_heads):
             assert list(idx[j, g]) == list(cand[:cfg.passing_len])
+
+
+# ------------------------------------------------- seeded random shapes, other paths
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_overlap_layer(seed):
+    cfg = _random_config(100 + seed).with_(dtype="bf16")
+    x = make_inputs(cfg)
+    got = _gpu_overlap(cfg, x)
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    _check_selection(cfg, got, ref)
+    _check_full(cfg, got, ref)
+    two, _ = _gpu_run(cfg, x)
+    assert np.array_equal(got["idx"], two["idx"])
+    assert np.array_equal(got["scores"], two["scores"])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_query_block(seed):
+    import random
+    base = _random_config(200 + seed)
+    nq = random.Random(7000 + seed).randint(1, 400)
+    n_ctx = base.seq_len
+    cfg = base.with_(seq_len=n_ctx + nq)
+    x = make_inputs(cfg)
+    ctx, qry = _query_case(cfg, x, context=n_ctx)
+    cfg_ctx = cfg.with_(seq_len=n_ctx)
+    out, lse = _gpu_query(cfg_ctx, ctx, qry)
+    ro, rl = oracle.query_block_attention(oracle.shape_of(cfg_ctx), qry["q"], qry["k"], qry["v"],
+                                          ctx["k"], ctx["v"])
+    o_tol, l_tol = TOL[cfg.dtype]
+    assert np.abs(out - ro).max() <= o_tol
+    assert np.abs(lse - rl).max() <= l_tol
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_query_aware_selection(seed):
+    import random
+    cfg = _random_config(300 + seed)
+    nq = random.Random(8000 + seed).randint(1, 300)
+    x = make_inputs(cfg)
+    qcfg = cfg.with_(seq_len=nq, num_hosts=1, anchor_len=0, window=1, seed=cfg.seed + 500)
+    q_qr = make_inputs(qcfg)["q"]
+    idx, sc = _gpu_query_select(cfg, x, q_qr)
+    sh = oracle.shape_of(cfg)
+    ref_sc = oracle.all_query_scores(sh, q_qr, x["k"])
+    ref_idx = oracle.select_passing(sh, ref_sc)
+    _check_selection(cfg, {"idx": idx, "scores": sc}, {"idx": ref_idx, "scores": ref_sc})
