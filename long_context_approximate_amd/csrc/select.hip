@@ -11,8 +11,8 @@
 // Observers are the last w queries of each block (causal), or, for the query-aware
 // variant, the rows of a query block that follows the context (every key visible).
 //
-//   rowstats  (m, z) = (max logit, sum exp(logit - max)) of every observer row over
-//             one key split; float64 dot products on v_mfma_f64_16x16x4_f64. When
+//   rowstats  (m, z) = (reference, sum exp(logit - reference)) of every observer row
+//             over one key split, the reference within 64 of the row's largest logit; float64 dot products on v_mfma_f64_16x16x4_f64. When
 //             the plan stores logits, the scaled float64 logits are written too;
 //   merge     combine the key splits of each row into (m, 1/z);
 //   colsum    per key: sum over all observer rows of exp(x - m) / z, in one fixed
@@ -159,23 +159,23 @@ __device__ inline void load_keys(const Plan& p, const T* k, int g, int64_t key0,
   }
 }
 
-// exp(y) for y <= 0 in float64, within 2 ulp. Every exponent on the hot paths is a
-// logit minus a running or final row maximum, so it is never positive. Tang's
-// table-driven method: y = (64 n + j) ln2/64 + r with |r| <= ln2/128, so
+// exp(y) in float64 for y <= 709, within 2 ulp; 0 below -745.2 (and for y = -inf).
+// Tang's table-driven method: y = (64 n + j) ln2/64 + r with |r| <= ln2/128, so
 // exp(y) = 2^n * 2^(j/64) * exp(r); 2^(j/64) comes from a 64-entry table in LDS and
 // exp(r) from its degree-5 Taylor polynomial (truncation error below 2^-54, a sixth of
-// an ulp of 1). ln2/64 is
-// split into a 36-bit head (exact products k * head for |k| < 2^17) and a tail.
-// Arguments below -745.2 underflow to 0.
+// an ulp of 1). ln2/64 is split into a 36-bit head (exact products k * head for
+// |k| < 2^17) and a tail. Branch-free: the argument is clamped to -746 so the
+// arithmetic stays finite, and the underflow is a final select, so a run of calls
+// issues its table reads together.
 constexpr int kExpTab = 64;
 __device__ inline void init_exp_table(double* tab) {
   if (threadIdx.x < kExpTab) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) / kExpTab);
   __syncthreads();
 }
-__device__ inline double exp_nonpos(double y, const double* tab) {
-  if (!(y > -745.2)) return 0.0;
-  const double k = rint(y * 0x1.71547652b82fep+6);          // y * 64 / ln2
-  double r = fma(-k, 0x1.62e42fefa0000p-7, y);              // head of ln2 / 64
+__device__ inline double exp_tab(double y, const double* tab) {
+  const double yc = fmax(y, -746.0);
+  const double k = rint(yc * 0x1.71547652b82fep+6);         // y * 64 / ln2
+  double r = fma(-k, 0x1.62e42fefa0000p-7, yc);             // head of ln2 / 64
   r = fma(-k, 0x1.cf79abc9e3b3ap-46, r);                    // tail
   double a = fma(r, 1.0 / 120.0, 1.0 / 24.0);
   a = fma(r, a, 1.0 / 6.0);
@@ -183,8 +183,16 @@ __device__ inline double exp_nonpos(double y, const double* tab) {
   a = fma(r, a, 1.0);
   const double er = fma(r, a, 1.0);
   const int ki = static_cast<int>(k);
-  return ldexp(tab[ki & (kExpTab - 1)] * er, ki >> 6);
+  const double v = ldexp(tab[ki & (kExpTab - 1)] * er, ki >> 6);
+  return yc > -745.2 ? v : 0.0;
 }
+
+// Row statistics keep a lazy reference instead of the running maximum: the reference is
+// raised only when a tile's largest logit exceeds it by more than this margin (the
+// first tile, or a far larger logit), so the common path has no rescaling branch.
+// Terms exp(x - ref) stay below e^64 and a row's sum below 2^105: no overflow, and the
+// relative rounding of a float64 sum does not depend on its scale.
+constexpr double kRefMargin = 64.0;
 
 // The stored logits are written once and read once (3.3 GB at 128K tokens, far past
 // the caches): both passes use non-temporal accesses so the stream does not evict
@@ -199,8 +207,8 @@ __device__ inline double2 nt_load2(const double* ptr) {
 __device__ inline void lse_merge(double& m, double& z, double mo, double zo, const double* tab) {
   const double mn = fmax(m, mo);
   if (mn == -INFINITY) return;  // both empty
-  const double a = (m == -INFINITY) ? 0.0 : z * exp_nonpos(m - mn, tab);
-  const double b = (mo == -INFINITY) ? 0.0 : zo * exp_nonpos(mo - mn, tab);
+  const double a = (m == -INFINITY) ? 0.0 : z * exp_tab(m - mn, tab);
+  const double b = (mo == -INFINITY) ? 0.0 : zo * exp_tab(mo - mn, tab);
   z = a + b;
   m = mn;
 }
@@ -278,13 +286,13 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
             __builtin_nontemporal_store(x1, row + 16 + col);
           }
           const double mt = fmax(x0, x1);
-          if (mt > m[rb][rr]) {
+          if (mt > m[rb][rr] + kRefMargin) {
             z[rb][rr] =
-                (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp_nonpos(m[rb][rr] - mt, etab);
+                (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp_tab(m[rb][rr] - mt, etab);
             m[rb][rr] = mt;
           }
-          z[rb][rr] += exp_nonpos(x0 - m[rb][rr], etab);
-          z[rb][rr] += exp_nonpos(x1 - m[rb][rr], etab);
+          z[rb][rr] += exp_tab(x0 - m[rb][rr], etab);
+          z[rb][rr] += exp_tab(x1 - m[rb][rr], etab);
         }
       continue;
     }
@@ -305,13 +313,14 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
             __builtin_nontemporal_store(
                 x[kb], lg + static_cast<int64_t>(r0 + rb * 16 + 4 * rr + kg) * p.nb + (key - s));
         }
-        if (mt > m[rb][rr]) {
-          z[rb][rr] = (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp_nonpos(m[rb][rr] - mt, etab);
+        if (mt > m[rb][rr] + kRefMargin) {
+          z[rb][rr] = (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp_tab(m[rb][rr] - mt, etab);
           m[rb][rr] = mt;
         }
+        // Hidden keys add exp(-inf) = 0 (x - m is never formed with m = -inf for them).
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          if (vis[kb]) z[rb][rr] += exp_nonpos(x[kb] - m[rb][rr], etab);
+          z[rb][rr] += exp_tab(vis[kb] ? x[kb] - m[rb][rr] : -INFINITY, etab);
       }
   }
   // Reduce over the 16 lanes (l % 16) that hold different keys of the same rows.
@@ -348,12 +357,12 @@ __global__ void merge_kernel(Plan p, const double2* __restrict__ part,
     const double2 pr = part[(jg * p.KS + sidx) * p.R + r];
     lse_merge(m, z, pr.x, pr.y, etab);
   }
-  rowstat[t] = make_double2(m, 1.0 / z);   // (max, 1 / sum)
+  rowstat[t] = make_double2(m, 1.0 / z);   // (reference, 1 / sum)
 }
 
 // exp(x - m) / z of one visible (row, key), else 0 (the same code in both score passes).
 __device__ inline double prob_term(bool vis, double x, double2 mz, const double* etab) {
-  return vis ? exp_nonpos(x - mz.x, etab) * mz.y : 0.0;
+  return vis ? exp_tab(x - mz.x, etab) * mz.y : 0.0;
 }
 
 // The four lanes col, col+16, col+32, col+48 hold disjoint row sets of the same key;
