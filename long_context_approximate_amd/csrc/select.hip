@@ -213,9 +213,20 @@ __device__ inline void lse_merge(double& m, double& z, double mo, double zo, con
   m = mn;
 }
 
+// Stored logits are key-tile major: pair (jg - jg0), then 32-key tile t = (key - s_j)/32,
+// then row r, then the key's slot in the tile; a pair holds R * round_up(n_b, 32)
+// values. A row-statistics tile (32 rows x 32 keys) is one contiguous 8 KB block, and
+// the score pass streams a key tile's rows from one contiguous run.
+__device__ inline int64_t logit_pair_len(const Plan& p) {
+  return static_cast<int64_t>(p.R) * ((static_cast<int64_t>(p.nb) + 31) & ~int64_t(31));
+}
+__device__ inline int64_t logit_at(const Plan& p, int r, int64_t kk) {   // kk = key - s_j
+  return ((kk >> 5) * p.R + r) * 32 + (kk & 31);
+}
+
 // One wave per (jg, 32-row tile, key split) for the pairs [jg0, jg0 + npairs). Waves
 // are independent (no barriers). STORE: also write the scaled logits of every visible
-// (row, key) to logits[(jg - jg0)][r][key - s_j].
+// (row, key) to the stored-logit layout above.
 template <typename T, int D, bool STORE>
 __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restrict__ q,
                                                        const T* __restrict__ k,
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
   const int64_t split_lo = s + static_cast<int64_t>(split) * p.split_keys;
   const int64_t split_hi = min(s + p.nb, split_lo + p.split_keys);
   const int r0 = rt * kWaveRows;
-  double* lg = STORE ? logits + static_cast<int64_t>(jg - jg0) * p.R * p.nb : nullptr;
+  double* lg = STORE ? logits + static_cast<int64_t>(jg - jg0) * logit_pair_len(p) : nullptr;
 
   Frag<T, D> qa[2];
   load_rows<T, D>(p, q, j, g, r0, col, kg, qa);
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
         for (int rr = 0; rr < 4; ++rr) {
           const double x0 = p.scale * acc[rb][0][rr], x1 = p.scale * acc[rb][1][rr];
           if (STORE) {
-            double* row = lg + static_cast<int64_t>(r0 + rb * 16 + 4 * rr + kg) * p.nb + (key0 - s);
+            double* row = lg + logit_at(p, r0 + rb * 16 + 4 * rr + kg, key0 - s);   // slot 0
             __builtin_nontemporal_store(x0, row + col);
             __builtin_nontemporal_store(x1, row + 16 + col);
           }
@@ -311,7 +322,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
           if (vis[kb]) mt = fmax(mt, x[kb]);
           if (STORE && vis[kb])
             __builtin_nontemporal_store(
-                x[kb], lg + static_cast<int64_t>(r0 + rb * 16 + 4 * rr + kg) * p.nb + (key - s));
+                x[kb], lg + logit_at(p, r0 + rb * 16 + 4 * rr + kg, key - s));
         }
         if (mt > m[rb][rr] + kRefMargin) {
           z[rb][rr] = (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp_tab(m[rb][rr] - mt, etab);
@@ -458,14 +469,14 @@ __global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double
   const int64_t e = s + p.nb;
   const int64_t key0 = s + static_cast<int64_t>(kt) * kWaveKeys;
   // This lane holds two adjacent keys (one 16-byte load per row when both are
-  // visible and the rows are 16-byte aligned); the row order of every key's sum is
-  // that of colsum_kernel, so the scores are the same.
+  // visible); the row order of every key's sum is that of colsum_kernel, so the
+  // scores are the same. One load instruction covers 4 consecutive rows of the key
+  // tile: 1 KB contiguous.
   int64_t key[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) key[kb] = key0 + 2 * col + kb;
-  const bool pairs16 = (p.nb & 1) == 0;
   const double2* st = rowstat + static_cast<int64_t>(jg) * p.R;
-  const double* lg = logits + static_cast<int64_t>(jg - jg0) * p.R * p.nb;
+  const double* lg = logits + static_cast<int64_t>(jg - jg0) * logit_pair_len(p);
 
   // Keys every observer row sees (window rows sit at e - w .. e - 1 and see keys up
   // to their own position; query-block rows see the whole block): row tiles without
@@ -473,14 +484,14 @@ __global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double
   const bool keys_full = p.obs_query ? key0 + kWaveKeys <= e : key0 + kWaveKeys - 1 <= e - p.w;
   double colsum[2] = {0.0, 0.0};
   for (int r0 = 0; r0 < p.R; r0 += kWaveRows) {
-    if (keys_full && pairs16 && r0 + kWaveRows <= p.R) {
+    if (keys_full && r0 + kWaveRows <= p.R) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int r = r0 + rb * 16 + 4 * rr + kg;
           const double2 mz = st[r];
-          const double2 t = nt_load2(lg + static_cast<int64_t>(r) * p.nb + (key[0] - s));
+          const double2 t = nt_load2(lg + logit_at(p, r, key[0] - s));
           colsum[0] += prob_term(true, t.x, mz, etab);
           colsum[1] += prob_term(true, t.y, mz, etab);
         }
@@ -496,9 +507,9 @@ __global__ __launch_bounds__(256) void colsum_stored_kernel(Plan p, const double
         const int64_t qi = ok ? row_key_limit(p, j, r) : -1;
         const bool v0 = key[0] <= qi && key[0] < e;
         const bool v1 = key[1] <= qi && key[1] < e;   // implies v0
-        const double* row = lg + static_cast<int64_t>(r) * p.nb + (key[0] - s);
+        const double* row = lg + logit_at(p, ok ? r : 0, key[0] - s);
         double x0 = 0.0, x1 = 0.0;
-        if (v1 && pairs16) {
+        if (v1) {
           const double2 t = nt_load2(row);
           x0 = t.x;
           x1 = t.y;

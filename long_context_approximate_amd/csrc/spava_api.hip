@@ -143,10 +143,12 @@ void set_select_layout(Plan* p) {
   p->KS = static_cast<int>(cdiv(p->nb, p->split_keys));
   const char* e = getenv("SPAVA_SELECT_LOGITS");
   const bool recompute = e && strcmp(e, "recompute") == 0;
-  // R * nb * 8 <= kLogitPairBytes, tested without forming the (possibly huge) product.
-  const bool small = p->R <= kLogitPairBytes / (static_cast<int64_t>(sizeof(double)) * p->nb);
+  // A pair's stored logits: R rows of round_up(nb, 32) values (32-key tiles).
+  // R * nbp * 8 <= kLogitPairBytes, tested without forming the (possibly huge) product.
+  const int64_t nbp = round_up(p->nb, 32);
+  const bool small = p->R <= kLogitPairBytes / (static_cast<int64_t>(sizeof(double)) * nbp);
   const int64_t per_pair =
-      small ? static_cast<int64_t>(p->R) * p->nb * static_cast<int64_t>(sizeof(double)) : 0;
+      small ? static_cast<int64_t>(p->R) * nbp * static_cast<int64_t>(sizeof(double)) : 0;
   p->store_logits = (!recompute && jg > 0 && small) ? 1 : 0;
   p->pair_chunk = p->store_logits
                       ? static_cast<int>(std::max<int64_t>(1, std::min(jg, kLogitChunkBytes / per_pair)))
@@ -160,8 +162,8 @@ SelectWs select_ws_layout(const Plan& p) {
   w.rowstat_part = region(cur, jg * p.KS * p.R * 2 * sizeof(double));
   w.rowstat = region(cur, jg * p.R * 2 * sizeof(double));
   w.scores = region(cur, jg * p.nb * sizeof(double));
-  w.logits = region(cur, p.store_logits ? static_cast<size_t>(p.pair_chunk) * p.R * p.nb *
-                                              sizeof(double)
+  w.logits = region(cur, p.store_logits ? static_cast<size_t>(p.pair_chunk) * p.R *
+                                              round_up(p.nb, 32) * sizeof(double)
                                         : 0);
   w.total = cur;
   return w;

@@ -82,9 +82,9 @@ def test_null_shape(lib):
 
 
 def _logit_bytes(jg, R, nb):
-    """Stored float64 logits: one chunk of (block, KV head) pairs when a pair fits in
-    512 MiB, at most 4 GiB per chunk; none otherwise."""
-    per_pair = R * nb * 8
+    """Stored float64 logits (R rows of 32-key tiles per pair): one chunk of (block, KV
+    head) pairs when a pair fits in 512 MiB, at most 4 GiB per chunk; none otherwise."""
+    per_pair = R * (-(-nb // 32) * 32) * 8
     if jg == 0 or per_pair > (512 << 20):
         return 0
     return max(1, min(jg, (4 << 30) // per_pair)) * per_pair
