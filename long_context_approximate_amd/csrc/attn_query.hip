@@ -224,7 +224,8 @@ template <typename T, typename L>
 __global__ __launch_bounds__(256) void query_merge_kernel(Plan p, int64_t nq,
                                                           const float* __restrict__ part_o,
                                                           const L* __restrict__ part_lse,
-                                                          T* __restrict__ out, float* __restrict__ lse) {
+                                                          T* __restrict__ out,
+                                                          float* __restrict__ lse) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int dq = p.D / 4;
   if (t >= nq * p.Hq * dq) return;
@@ -276,8 +277,9 @@ hipError_t launch_query_bf16(const Plan& p, int64_t nq, const uint16_t* q_qr, co
   hipLaunchKernelGGL(query_partial_kernel<D>, dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0,
                      st, p, nq, qtiles, NG, q_qr, k_qr, k, vtctx, vtq, part_o, part_lse, c_log2);
   const int64_t threads = nq * p.Hq * (p.D / 4);
-  hipLaunchKernelGGL((query_merge_kernel<uint16_t, float>), dim3(static_cast<unsigned>(cdiv(threads, 256))),
-                     dim3(256), 0, st, p, nq, part_o, part_lse, out, lse);
+  const dim3 mgrid(static_cast<unsigned>(cdiv(threads, 256)));
+  hipLaunchKernelGGL((query_merge_kernel<uint16_t, float>), mgrid, dim3(256), 0, st, p, nq, part_o,
+                     part_lse, out, lse);
   return hipGetLastError();
 }
 
@@ -293,8 +295,9 @@ hipError_t launch_query_f32(const Plan& p, int64_t nq, const float* q_qr, const 
                      dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq), dim3(64), 0, st, p, nq,
                      qtiles, q_qr, k_qr, v_qr, k, v, part_o, part_lse);
   const int64_t threads = nq * p.Hq * (p.D / 4);
-  hipLaunchKernelGGL((query_merge_kernel<float, double>), dim3(static_cast<unsigned>(cdiv(threads, 256))),
-                     dim3(256), 0, st, p, nq, part_o, part_lse, out, lse);
+  const dim3 mgrid(static_cast<unsigned>(cdiv(threads, 256)));
+  hipLaunchKernelGGL((query_merge_kernel<float, double>), mgrid, dim3(256), 0, st, p, nq, part_o,
+                     part_lse, out, lse);
   return hipGetLastError();
 }
 

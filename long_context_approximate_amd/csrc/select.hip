@@ -12,8 +12,9 @@
 // variant, the rows of a query block that follows the context (every key visible).
 //
 //   rowstats  (m, z) = (reference, sum exp(logit - reference)) of every observer row
-//             over one key split, the reference within 64 of the row's largest logit; float64 dot products on v_mfma_f64_16x16x4_f64. When
-//             the plan stores logits, the scaled float64 logits are written too;
+//             over one key split, the reference within 64 of the row's largest
+//             logit; float64 dot products on v_mfma_f64_16x16x4_f64. When the plan
+//             stores logits, the scaled float64 logits are written too;
 //   merge     combine the key splits of each row into (m, 1/z);
 //   colsum    per key: sum over all observer rows of exp(x - m) / z, in one fixed
 //             order for every key (so equal keys get bitwise-equal scores), then
