@@ -1,12 +1,12 @@
-// Approximate attention, float32 inputs (plain float32 VALU path).
+// Approximate attention, float32 inputs (VALU path, float64 arithmetic).
 //
 // Same visible set as the bf16 path (explainer "APB-V: ...", Methodik >
 // Approximativer Attention-Mechanismus > Berechnung): anchor + passing rows of the
-// earlier blocks, then the block's own causal keys. Every product, exponential and
-// sum is float32 except the softmax denominator, which is summed in float64. One
-// thread owns one query row; a workgroup of 64 threads covers 64
-// consecutive queries of one head and streams 64-key K/V tiles through LDS.
-#include "spava_internal.h"
+// earlier blocks, then the block's own causal keys. Float64 arithmetic except the
+// float32 exponentials (see F32Row). A workgroup of two waves covers 64 consecutive
+// queries of one head, each row on a lane pair, and streams 64-key K/V tiles
+// through LDS.
+#include "attn_f32_step.h"
 
 namespace spava {
 namespace {
@@ -57,17 +57,17 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(Plan p, const float* __re
   }
 }
 
-// grid (H * ceil(nb/64), Hq), block 64.
+// grid (H * ceil(nb/64), Hq), block 128: two waves of 32 query rows, each row held by
+// a lane pair (see F32Row).
 template <int D>
-__global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float* __restrict__ q,
-                                                      const float* __restrict__ k,
-                                                      const float* __restrict__ v,
-                                                      const float* __restrict__ kpre,
-                                                      const float* __restrict__ vpre,
-                                                      float* __restrict__ out,
-                                                      float* __restrict__ lse) {
-  __shared__ float Ks[BN][D + 1];
-  __shared__ float Vs[BN][D + 1];
+__global__ __launch_bounds__(128) void attn_f32_kernel(Plan p, const float* __restrict__ q,
+                                                       const float* __restrict__ k,
+                                                       const float* __restrict__ v,
+                                                       const float* __restrict__ kpre,
+                                                       const float* __restrict__ vpre,
+                                                       float* __restrict__ out,
+                                                       float* __restrict__ lse) {
+  __shared__ F32Tile<D> tile;
   const int tiles_per_block = (p.nb + BN - 1) / BN;
   const int h = blockIdx.x / tiles_per_block;
   const int qt = blockIdx.x % tiles_per_block;
@@ -75,21 +75,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float* __res
   const int g = hq / p.G;
   const int tid = threadIdx.x;
   const int64_t s_h = static_cast<int64_t>(h) * p.nb, e_h = s_h + p.nb;
-  const int64_t qi = s_h + static_cast<int64_t>(qt) * BN + tid;
+  const int64_t qi = s_h + static_cast<int64_t>(qt) * BN + (tid >> 6) * 32 + (tid & 31);
   const bool valid = qi < e_h;
   const int64_t q_last = min(s_h + static_cast<int64_t>(qt + 1) * BN, e_h) - 1;
-  const float scale = static_cast<float>(p.scale);
 
-  float qr[D], acc[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qr[d] = valid ? q[qi * p.qs_tok + hq * p.qs_head + d] : 0.f;
-    acc[d] = 0.f;
-  }
-  // The denominator is summed in float64: in float32, weights below half an ulp of the
-  // running sum would be dropped, all in the same direction.
-  float m = -INFINITY;
-  double l = 0.0;
+  F32Row<D> row;
+  row.init(valid ? q + qi * p.qs_tok + hq * p.qs_head : nullptr);
 
   const int L = prefix_len(p, h);
   const int npre = (L + BN - 1) / BN;
@@ -98,51 +89,26 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float* __res
     const bool local = it >= npre;
     const int64_t key0 = local ? s_h + static_cast<int64_t>(it - npre) * BN : it * BN;
     __syncthreads();
-    for (int c = tid; c < BN * D; c += 64) {
-      const int row = c / D, d = c % D;
-      float kv = 0.f, vv = 0.f;
-      if (local) {
-        const int64_t key = key0 + row;
-        if (key < e_h) {
-          kv = k[key * p.kvs_tok + g * p.kvs_head + d];
-          vv = v[key * p.kvs_tok + g * p.kvs_head + d];
-        }
-      } else {
-        const int64_t off = (static_cast<int64_t>(g) * p.Lpad + key0 + row) * D + d;
-        kv = kpre[off];
-        vv = vpre[off];
-      }
-      Ks[row][d] = kv;
-      Vs[row][d] = vv;
+    if (local) {
+      f32_load_tile<D>(
+          tile, static_cast<int>(min<int64_t>(BN, e_h - key0)),
+          [&](int r) { return k + (key0 + r) * p.kvs_tok + g * p.kvs_head; },
+          [&](int r) { return v + (key0 + r) * p.kvs_tok + g * p.kvs_head; }, 128);
+    } else {
+      const int64_t base = static_cast<int64_t>(g) * p.Lpad + key0;
+      f32_load_tile<D>(
+          tile, BN, [&](int r) { return kpre + (base + r) * D; },
+          [&](int r) { return vpre + (base + r) * D; }, 128);
     }
     __syncthreads();
-    for (int kk = 0; kk < BN; ++kk) {
-      const int64_t key = key0 + kk;
-      const bool vis = local ? (key <= qi) : (key < L);
-      if (!vis) continue;
-      float dot = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) dot = fmaf(qr[d], Ks[kk][d], dot);
-      const float x = dot * scale;
-      if (x > m) {
-        const float alpha = expf(m - x);   // m = -inf gives 0
-#pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] *= alpha;
-        l *= static_cast<double>(alpha);
-        m = x;
-      }
-      const float pe = expf(x - m);
-      l += static_cast<double>(pe);
-#pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(pe, Vs[kk][d], acc[d]);
-    }
+    // Visible keys of the tile form a prefix: the prefix rows below L, or the causal
+    // keys up to the query itself.
+    const int64_t lim = local ? qi - key0 : static_cast<int64_t>(L) - key0 - 1;
+    row.step(tile, valid ? static_cast<int>(min<int64_t>(lim, BN - 1)) : -1, p.scale);
   }
   if (!valid) return;
-  const float inv = static_cast<float>(1.0 / l);
-#pragma unroll
-  for (int d = 0; d < D; ++d) out[qi * p.os_tok + hq * p.os_head + d] = acc[d] * inv;
-  if (lse)
-    lse[static_cast<int64_t>(hq) * p.N + qi] = static_cast<float>(static_cast<double>(m) + log(l));
+  row.store(out + qi * p.os_tok + hq * p.os_head);
+  if (lse && row.half == 0) lse[static_cast<int64_t>(hq) * p.N + qi] = static_cast<float>(row.lse());
 }
 
 template <int D>
@@ -155,8 +121,8 @@ hipError_t launch_f32_d(const Plan& p, const float* q, const float* k, const flo
     hipLaunchKernelGGL(prep_f32_kernel<D>, dim3(p.Lpad / BN, p.Hkv), dim3(256), 0, st, p, k, v,
                        idx, kpre, vpre);
   const unsigned gx = static_cast<unsigned>(p.H * cdiv(p.nb, BN));
-  hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(gx, p.Hq), dim3(64), 0, st, p, q, k, v, kpre, vpre,
-                     out, lse);
+  hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(gx, p.Hq), dim3(128), 0, st, p, q, k, v, kpre,
+                     vpre, out, lse);
   return hipGetLastError();
 }
 

@@ -12,9 +12,11 @@
 //   vt_rows    V^T tiles (MFMA slot order) of the context blocks and of the query keys;
 //   partial    bf16: one workgroup = 256 query rows x 1 head x 1 partial (H context
 //              blocks + the query block itself), the same flash step as the main
-//              attention; f32: one thread per query row, float32 VALU;
+//              attention; f32: each query row on a lane pair, float64 arithmetic
+//              except the float32 exponentials;
 //   merge      O = sum_h exp(LSE_h - LSE) O_h with LSE = log sum_h exp(LSE_h).
 #include "attn_common.h"
+#include "attn_f32_step.h"
 
 namespace spava {
 namespace {
@@ -133,80 +135,44 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
   }
 }
 
-// float32 inputs: one thread per query row; grid ((H + 1) * ceil(nq / 64), Hq), 64 threads.
+// float32 inputs: each query row on a lane pair (see F32Row); grid
+// ((H + 1) * ceil(nq / 64), Hq), two waves of 32 rows.
 template <int D>
-__global__ __launch_bounds__(64) void query_partial_f32_kernel(
+__global__ __launch_bounds__(128) void query_partial_f32_kernel(
     Plan p, int64_t nq, int qtiles, const float* __restrict__ q_qr, const float* __restrict__ k_qr,
     const float* __restrict__ v_qr, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ part_o, double* __restrict__ part_lse) {
-  __shared__ float Ks[BN][D + 1];
-  __shared__ float Vs[BN][D + 1];
+  __shared__ F32Tile<D> tile;
   const int ph = blockIdx.x / qtiles, qt = blockIdx.x % qtiles;
   const int hq = blockIdx.y, g = hq / p.G;
   const bool self = ph == p.H;
   const int tid = threadIdx.x;
-  const int64_t qi = static_cast<int64_t>(qt) * BN + tid;
+  const int64_t qi = static_cast<int64_t>(qt) * BN + (tid >> 6) * 32 + (tid & 31);
   const bool valid = qi < nq;
   const int64_t q_last = min(static_cast<int64_t>(qt + 1) * BN, nq) - 1;
-  const float scale = static_cast<float>(p.scale);
   const float* kb = self ? k_qr : k + static_cast<int64_t>(ph) * p.nb * p.kvs_tok;
   const float* vb = self ? v_qr : v + static_cast<int64_t>(ph) * p.nb * p.kvs_tok;
   const int64_t nkeys = self ? q_last + 1 : p.nb;
 
-  float qr[D], acc[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qr[d] = valid ? q_qr[qi * p.qs_tok + hq * p.qs_head + d] : 0.f;
-    acc[d] = 0.f;
-  }
-  // The denominator is summed in float64: in float32, weights below half an ulp of the
-  // running sum would be dropped, all in the same direction.
-  float m = -INFINITY;
-  double l = 0.0;
+  F32Row<D> row;
+  row.init(valid ? q_qr + qi * p.qs_tok + hq * p.qs_head : nullptr);
   for (int64_t key0 = 0; key0 < nkeys; key0 += BN) {
     __syncthreads();
-    for (int c = tid; c < BN * D; c += 64) {
-      const int row = c / D, d = c % D;
-      const int64_t key = key0 + row;
-      float kv = 0.f, vv = 0.f;
-      if (key < nkeys) {
-        kv = kb[key * p.kvs_tok + g * p.kvs_head + d];
-        vv = vb[key * p.kvs_tok + g * p.kvs_head + d];
-      }
-      Ks[row][d] = kv;
-      Vs[row][d] = vv;
-    }
+    f32_load_tile<D>(
+        tile, static_cast<int>(min<int64_t>(BN, nkeys - key0)),
+        [&](int r) { return kb + (key0 + r) * p.kvs_tok + g * p.kvs_head; },
+        [&](int r) { return vb + (key0 + r) * p.kvs_tok + g * p.kvs_head; }, 128);
     __syncthreads();
-    for (int kk = 0; kk < BN; ++kk) {
-      const int64_t key = key0 + kk;
-      const bool vis = key < nkeys && (!self || key <= qi);
-      if (!vis) continue;
-      float dot = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) dot = fmaf(qr[d], Ks[kk][d], dot);
-      const float x = dot * scale;
-      if (x > m) {
-        const float alpha = expf(m - x);
-#pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] *= alpha;
-        l *= static_cast<double>(alpha);
-        m = x;
-      }
-      const float pe = expf(x - m);
-      l += static_cast<double>(pe);
-#pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(pe, Vs[kk][d], acc[d]);
-    }
+    // Visible keys form a prefix of the tile: all present keys of a context block, the
+    // query keys up to the row itself.
+    int64_t lim = nkeys - 1 - key0;
+    if (self) lim = min(lim, qi - key0);
+    row.step(tile, valid ? static_cast<int>(min<int64_t>(lim, BN - 1)) : -1, p.scale);
   }
   if (!valid) return;
-  const float inv = static_cast<float>(1.0 / l);
-  float* op = part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * D;
-#pragma unroll
-  for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
-  // The partial's LSE is kept in float64: the merge weights exp(LSE_h - LSE) would
-  // otherwise carry the float32 rounding of LSE values of magnitude ~10-50.
-  part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] =
-      static_cast<double>(m) + log(l);
+  row.store(part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * D);
+  // The partial's LSE is kept in float64 for the merge weights exp(LSE_h - LSE).
+  if (row.half == 0) part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] = row.lse();
 }
 
 __device__ inline void store4(uint16_t* dst, float4 v) {
@@ -292,8 +258,8 @@ hipError_t launch_query_f32(const Plan& p, int64_t nq, const float* q_qr, const 
   double* part_lse = reinterpret_cast<double*>(ws + w.part_lse);
   const int qtiles = static_cast<int>(cdiv(nq, BN));
   hipLaunchKernelGGL(query_partial_f32_kernel<D>,
-                     dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq), dim3(64), 0, st, p, nq,
-                     qtiles, q_qr, k_qr, v_qr, k, v, part_o, part_lse);
+                     dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq), dim3(128), 0, st, p,
+                     nq, qtiles, q_qr, k_qr, v_qr, k, v, part_o, part_lse);
   const int64_t threads = nq * p.Hq * (p.D / 4);
   const dim3 mgrid(static_cast<unsigned>(cdiv(threads, 256)));
   hipLaunchKernelGGL((query_merge_kernel<float, double>), mgrid, dim3(256), 0, st, p, nq, part_o,

@@ -81,6 +81,13 @@ SMALL = [
     small_config(name="G7_tail", seq_len=2600, num_hosts=2, num_q_heads=7, num_kv_heads=1,
                  anchor_len=1, passing_len=513, window=129, seed=11),
     small_config(name="t3_keys", seq_len=2048, num_hosts=4, dist="student_t3", seed=12),
+    # float32 with heavy-tailed keys: dominant logits leave many weights below half an
+    # ulp of the running softmax denominator (summed in float64 for that reason).
+    small_config(name="f32_t3_keys", dtype="f32", seq_len=3000, num_hosts=3,
+                 dist="student_t3", seed=15),
+    small_config(name="f32_t3_long_d64", dtype="f32", head_dim=64, seq_len=4096, num_hosts=2,
+                 num_q_heads=4, num_kv_heads=1, anchor_len=128, passing_len=256, window=96,
+                 dist="student_t3", seed=16),
     # MHA (G = 1) with an odd head count, five hosts, a one-query window.
     small_config(name="mha_h5_w1", seq_len=3500, num_hosts=5, num_q_heads=3, num_kv_heads=3,
                  anchor_len=64, passing_len=200, window=1, seed=13),
