@@ -162,7 +162,8 @@ spava_status spava_select_passing(const spava_shape* shape, const void* q, const
  *   out[i, hq, :] = sum_p softmax_p(sm_scale * <q_i, k_p>) v_p over that set
  *   lse_out[hq, i] = log sum_p exp(sm_scale * <q_i, k_p>)   (natural log)
  * bf16 inputs use bf16 matrix cores with float32 accumulation and softmax, and
- * round `out` to bf16 (nearest even); f32 inputs compute in float32.
+ * round `out` to bf16 (nearest even); f32 inputs compute logits, softmax sums and O
+ * in float64 (exponentials in float32) and round `out` to float32.
  *
  *   q, k, v      device, dtype per shape (read only)
  *   passing_idx  device int32 [max(H-1,0), Hkv, l] as written by
