@@ -196,7 +196,7 @@ def _random_config(seed):
                         dist=r.choice(["normal", "student_t3"]), seed=6000 + seed)
 
 
-@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_shapes(seed):
     cfg = _random_config(seed)
     got, x = _gpu_run(cfg)
@@ -583,7 +583,7 @@ def test_query_aware_ties_go_to_lower_positions():
 
 # ------------------------------------------------- seeded random shapes, other paths
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_random_shapes_overlap_layer(seed):
     cfg = _random_config(100 + seed).with_(dtype="bf16")
     x = make_inputs(cfg)
@@ -596,7 +596,7 @@ def test_random_shapes_overlap_layer(seed):
     assert np.array_equal(got["scores"], two["scores"])
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_random_shapes_query_block(seed):
     import random
     base = _random_config(200 + seed)
@@ -614,7 +614,7 @@ def test_random_shapes_query_block(seed):
     assert np.abs(lse - rl).max() <= l_tol
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_random_shapes_query_aware_selection(seed):
     import random
     cfg = _random_config(300 + seed)
