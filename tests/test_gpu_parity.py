@@ -253,7 +253,17 @@ def _sample_rows(cfg, rng):
 
 @pytest.mark.parametrize("name", ["h4_16k", "video_h8_64k", "h8_128k", "t3_h16_256k"])
 def test_full_size_selection_and_sampled_rows(name):
-    cfg = CONFIGS[name]
+    _full_size_check(CONFIGS[name])
+
+
+def test_full_size_f32_heavy_tails():
+    # The 16K workload in float32 with heavy-tailed keys: 4096-key blocks plus prefixes
+    # of up to 2560 rows through the float32 path, every selection and sampled rows.
+    _full_size_check(CONFIGS["h4_16k"].with_(name="h4_16k_f32_t3", dtype="f32",
+                                             dist="student_t3"))
+
+
+def _full_size_check(cfg):
     got, x = _gpu_run(cfg)
     sh = oracle.shape_of(cfg)
     scores = oracle.all_window_scores(sh, x["q"], x["k"])
