@@ -263,6 +263,12 @@ def test_full_size_f32_heavy_tails():
                                              dist="student_t3"))
 
 
+def test_full_size_f32_128k():
+    # The 128K workload in float32: rows of up to ~30K visible keys through the float32
+    # path (float64 sums), every selection and sampled rows.
+    _full_size_check(CONFIGS["h8_128k"].with_(name="h8_128k_f32", dtype="f32"))
+
+
 def _full_size_check(cfg):
     got, x = _gpu_run(cfg)
     sh = oracle.shape_of(cfg)
