@@ -365,3 +365,91 @@ def test_query_aware_scores_equal_window_scores_of_a_last_row_observer():
     q_qr = q[31:32].copy()                     # block 0 ends at 32
     qa = orc.all_query_scores(sh, q_qr, k)
     np.testing.assert_allclose(qa, win, rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------ input widening and margins
+
+def _bf16_value_from_definition(bits: int) -> float:
+    """Value of a bf16 bit pattern from the format's definition: 1 sign bit, 8 exponent
+    bits (bias 127), 7 fraction bits; exponent 0 is subnormal (2^-126 * f/128),
+    exponent 255 is infinity (f == 0) or NaN."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e, f = (bits >> 7) & 0xFF, bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+def test_bf16_widening_on_every_bit_pattern():
+    # All 65536 patterns: the oracle's widening must give the value torch's own bfloat16
+    # -> float64 conversion gives, and the value the format's definition gives, bit for
+    # bit (signed zeros, subnormals and infinities included; NaN stays NaN).
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = orc.bf16_bits_to_f64(bits)
+    via_to_f64 = orc.to_f64(bits)
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    defn = np.array([_bf16_value_from_definition(int(b)) for b in bits])
+    for name, ref in (("torch", lib), ("definition", defn)):
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), name
+        assert np.array_equal(got[~nan].view(np.uint64), ref[~nan].view(np.uint64)), name
+    assert np.array_equal(via_to_f64.view(np.uint64), got.view(np.uint64))
+    assert got.dtype == np.float64 and via_to_f64.dtype == np.float64
+
+
+def _margin_fraction(sh, scores, j, g):
+    """Relative gap between the l_j-th and (l_j + 1)-th largest candidate scores of
+    block j, in exact rational arithmetic; None when nothing is selected or nothing is
+    rejected. Candidates are listed from the definition: block j's positions, minus the
+    anchor [0, A) for block 0."""
+    nb, A, l = sh.block_len, sh.anchor_len, sh.passing_len
+    cand = [p for p in range(j * nb, (j + 1) * nb) if not (j == 0 and p < A)]
+    lj = min(l, len(cand))
+    if lj == 0 or lj == len(cand):
+        return None
+    vals = sorted((Fraction(float(scores[j, g, p - j * nb])) for p in cand), reverse=True)
+    return (vals[lj - 1] - vals[lj]) / vals[lj - 1]
+
+
+def test_selection_margins_worked_example():
+    # N = 12, H = 3 (blocks of 4), A = 2, l = 2, two KV heads. Block 0's candidates are
+    # positions 2, 3 only (the anchor is excluded), so l_0 = |C_0| and nothing is
+    # rejected: NaN. Block 1, head 0: scores 1/2, 1/8, 1/4, 1/8 -> sorted 1/2, 1/4,
+    # 1/8, 1/8; the 2nd (1/4) against the 3rd (1/8): (1/4 - 1/8) / (1/4) = 1/2.
+    # Block 1, head 1: a tie at the boundary (3/8, 1/8, 1/8, 1/8 -> 1/8 vs 1/8) gives 0.
+    # The anchor rows of block 0 carry a huge score that must not count.
+    sh = orc.Shape(12, 3, 2, 2, 4, 2, 2, 1)
+    scores = np.zeros((2, 2, 4))
+    scores[0, :, :] = [1e9, 1e9, 0.25, 0.75]
+    scores[1, 0, :] = [0.5, 0.125, 0.25, 0.125]
+    scores[1, 1, :] = [0.375, 0.125, 0.125, 0.125]
+    m = orc.selection_margins(sh, scores)
+    assert m.shape == (2, 2)
+    assert np.isnan(m[0]).all()
+    assert m[1, 0] == 0.5
+    assert m[1, 1] == 0.0
+    # l = 0: nothing is selected anywhere.
+    assert np.isnan(orc.selection_margins(orc.Shape(12, 3, 2, 2, 4, 2, 0, 1), scores)).all()
+    # One host: no block passes rows, so there is nothing to report.
+    assert orc.selection_margins(orc.Shape(4, 1, 2, 2, 4, 0, 2, 1), np.zeros((0, 2, 4))).shape \
+        == (0, 2)
+
+
+@pytest.mark.parametrize("A,l", [(0, 3), (5, 3), (5, 11), (3, 16), (0, 16), (7, 1)])
+def test_selection_margins_match_exact_rationals(A, l):
+    # Random positive scores (with repeated values, so ties occur), checked against the
+    # exact rational gap of the definition; NaN exactly where nothing is rejected.
+    rng = np.random.default_rng(100 + 7 * A + l)
+    sh = orc.Shape(48, 3, 4, 2, 8, A, l, 2)
+    scores = rng.choice(rng.random(9) + 0.01, size=(2, 2, 16))
+    m = orc.selection_margins(sh, scores)
+    for j in range(2):
+        for g in range(2):
+            ref = _margin_fraction(sh, scores, j, g)
+            if ref is None:
+                assert np.isnan(m[j, g]), (j, g)
+            else:
+                assert abs(Fraction(float(m[j, g])) - ref) <= abs(ref) * Fraction(1, 2 ** 50), \
+                    (j, g, float(m[j, g]), float(ref))
