@@ -90,13 +90,14 @@ def score_flops(cfg) -> float:
     return 2.0 * cfg.head_dim * max(H - 1, 0) * hkv * G * visits
 
 
-def cpu_baseline(cfg, x, budget_rows=16384, pairs_sampled=8):
+def _oracle_sample(cfg, x, budget_rows, pairs_sampled):
     """Time the fp64 oracle on a sample of the workload and extrapolate to the whole.
 
     Sample: the window scores + top-l of `pairs_sampled` (block, KV head) pairs, and
     `budget_rows` query rows of one head in the first, a middle and the last block.
     The whole-workload time is extrapolated pair-by-pair for selection and by the
     oracle's own per-row key count (L_h + n_b keys per row) for attention.
+    Returns (estimated seconds for the whole workload, measured seconds, description).
     """
     import numpy as np
 
@@ -119,7 +120,8 @@ def cpu_baseline(cfg, x, budget_rows=16384, pairs_sampled=8):
         idx[j, :, :lj] = cand[:lj]
     sample_cost = 0.0
     t_rows = 0.0
-    for h in sorted({0, H // 2, H - 1}):
+    blocks = sorted({0, H // 2, H - 1})
+    for h in blocks:
         s = h * nb
         rows = np.arange(s, s + min(budget_rows, nb))
         L = len(oracle.visible_prefix(sh, idx, h, 0))
@@ -132,24 +134,72 @@ def cpu_baseline(cfg, x, budget_rows=16384, pairs_sampled=8):
         L = len(oracle.visible_prefix(sh, idx, h, 0))
         total_cost += nb * (L + nb) * cfg.num_q_heads
     t_total = t_pair * pairs + t_rows * (total_cost / sample_cost)
+    measured = t_pair * n_pairs + t_rows
+    desc = (f"window scores + top-l of {n_pairs} of {pairs} (block, kv-head) pairs, and "
+            f"{min(budget_rows, nb)} query rows x 1 head in blocks {blocks}; extrapolated by "
+            f"pair count and by the oracle's per-row key count (measured {measured:.1f} s)")
+    return t_total, measured, desc
+
+
+def _blas_info():
+    """BLAS libraries numpy runs on and their thread counts (threadpoolctl)."""
     try:
+        import numpy  # noqa: F401  (loads the BLAS threadpoolctl inspects)
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:  # pragma: no cover
-        threads = 1
-    return {
-        "value": cfg.seq_len / t_total,
+        return {"blas": "unknown", "blas_threads": 1}
+    names = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in libs})
+    threads = max([int(i.get("num_threads", 1)) for i in libs] or [1])
+    return {"blas": ", ".join(names) or "none", "blas_threads": threads}
+
+
+def _single_core_oracle():
+    """The oracle on one host thread for the two smallest workloads: the 512-token one
+    in full (measured), the 16K one from a bounded sample (extrapolated)."""
+    import oracle
+    from long_context_approximate_amd.inputs import CONFIGS, make_inputs
+    out = {}
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return None
+    with threadpool_limits(limits=1):
+        tiny = CONFIGS["tiny_f32_512"]
+        xt = make_inputs(tiny)
+        t0 = time.perf_counter()
+        oracle.run(oracle.shape_of(tiny), xt["q"], xt["k"], xt["v"])
+        dt = time.perf_counter() - t0
+        out[tiny.name] = {"seconds": dt, "tokens_per_s": tiny.seq_len / dt, "kind": "measured",
+                          "sample": "the whole workload (selection + attention)"}
+        c2 = CONFIGS["h4_16k"]
+        x2 = make_inputs(c2)
+        est, measured, desc = _oracle_sample(c2, x2, budget_rows=4096, pairs_sampled=2)
+        out[c2.name] = {"seconds": est, "tokens_per_s": c2.seq_len / est,
+                        "kind": "extrapolated", "sample": desc}
+    return out
+
+
+def cpu_baseline(cfg, x, budget_rows=16384, pairs_sampled=8):
+    """The fp64 oracle on the host cores: a bounded sample of the benchmarked workload,
+    extrapolated (see _oracle_sample), with the BLAS it ran on, plus one-thread times of
+    the two smallest workloads."""
+    est, measured, desc = _oracle_sample(cfg, x, budget_rows, pairs_sampled)
+    blas = _blas_info()
+    rec = {
+        "value": cfg.seq_len / est,
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": int(blas["blas_threads"]),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: window scores + top-l of {n_pairs} of {pairs} "
-                   f"(block, kv-head) pairs, and {budget_rows} query rows x 1 head in blocks "
-                   f"{sorted({0, H // 2, H - 1})}; extrapolated by pair count and by the "
-                   f"oracle's per-row key count (measured {t_pair * n_pairs + t_rows:.1f} s, "
-                   f"whole workload est. {t_total:.0f} s)"),
-        "seconds_extrapolated": t_total,
+        "sample": f"fp64 numpy oracle: {desc}; whole workload est. {est:.0f} s",
+        "seconds_extrapolated": est,
+        "seconds_measured": measured,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "blas": blas["blas"],
+        "blas_threads": blas["blas_threads"],
     }
+    rec["single_core"] = _single_core_oracle()
+    return rec
 
 
 def _time_call(fn, stream, reps):
@@ -165,20 +215,16 @@ def _time_call(fn, stream, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def time_schedules(shape, q, k, v, idx, out, lse, ws, stream, reps=3):
-    """Attention-call time under each dispatch order (same results, different timing)."""
+def time_schedules(cfg, q, k, v, idx, out, lse, ws, stream, reps=3):
+    """Attention-call time under each dispatch order (the shape's schedule field; same
+    results, different timing)."""
     from long_context_approximate_amd import spava
     res = {}
-    prev = os.environ.get("SPAVA_SCHEDULE")
     for mode in ("lpt", "zigzag", "natural"):
-        os.environ["SPAVA_SCHEDULE"] = mode
+        shape = spava.shape_from_config(cfg, schedule=spava.SCHEDULES[mode])
         res[mode] = _time_call(
             lambda: spava.spava_approx_attn_fwd(shape, q, k, v, idx, out, lse, ws, stream),
             stream, reps)
-    if prev is None:
-        os.environ.pop("SPAVA_SCHEDULE", None)
-    else:
-        os.environ["SPAVA_SCHEDULE"] = prev
     return res
 
 
@@ -363,7 +409,7 @@ def main():
             _profile_field("prep_kernel", "dur_us")),
     }
     if not args.no_extras:
-        rec["schedules_attn_ms"] = time_schedules(shape, q, k, v, idx, out, lse, ws_attn, stream)
+        rec["schedules_attn_ms"] = time_schedules(cfg, q, k, v, idx, out, lse, ws_attn, stream)
         rec["dense_causal"] = dense_baseline(cfg, q, k, v, stream, t_step)
         rec["query_block"] = query_block_timing(cfg, shape, k, v, stream)
         rec["overlap"] = overlap_timing(shape, q, k, v, idx, out, lse, stream, t_step)

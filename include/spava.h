@@ -21,17 +21,10 @@
  * spava_layer_overlap_fwd does the two calls of a layer at once, overlapping the
  * selection with the part of the attention that needs no passing rows.
  *
- * The environment variable SPAVA_SCHEDULE (lpt | natural | zigzag) selects the
- * dispatch order of the attention's query tiles: longest first (default), block
- * order, or the pages' ZigZag host pairing (h, H-1-h). It changes timing only,
- * never results.
- *
- * The selection keeps the float64 logits of its first pass for its second pass when
- * one (block, KV head) pair's logits take at most 512 MiB (G * w * n_b * 8 bytes),
- * processing pairs in chunks of at most 4 GiB of logits; otherwise, or with the
- * environment variable SPAVA_SELECT_LOGITS=recompute, it recomputes them. The
- * workspace size depends on this choice, so the size query and the call must see the
- * same environment. Scores are bitwise the same either way.
+ * Two execution choices travel in the shape struct, never in process state: the
+ * dispatch order of the attention's query tiles (spava_shape.schedule) and whether
+ * the selection keeps or recomputes its float64 logits (spava_shape.select_logits).
+ * Neither changes any result. The library reads no environment variable.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
@@ -65,10 +58,37 @@ typedef enum {
   SPAVA_ERR_ALIGN = 4,      /* pointer or stride not 16-byte aligned                */
   SPAVA_ERR_WORKSPACE = 5,  /* workspace smaller than the size query returned       */
   SPAVA_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed           */
-  SPAVA_ERR_DEVICE = 7      /* current device is not gfx950                         */
+  SPAVA_ERR_DEVICE = 7,     /* current device is not gfx950                         */
+  SPAVA_ERR_OPTION = 8      /* schedule or select_logits holds an unknown value      */
 } spava_status;
 
 typedef enum { SPAVA_BF16 = 0, SPAVA_F32 = 1 } spava_dtype;
+
+/*
+ * Dispatch order of the attention's (block, query tile) work items
+ * (spava_shape.schedule). Outputs are bitwise the same under every order; only the
+ * time differs. The explainer's load balancing ("Systemseitige Optimierungen":
+ * ZigZag pairing of hosts h and H-1-h so every host carries the same work) becomes,
+ * on one GPU, an order in which the hardware dispatcher takes the longest items first.
+ */
+typedef enum {
+  SPAVA_SCHED_LONGEST_FIRST = 0,  /* decreasing key-tile count, ties by index (default) */
+  SPAVA_SCHED_NATURAL = 1,        /* block-major                                        */
+  SPAVA_SCHED_ZIGZAG = 2          /* blocks paired (p, H-1-p), tiles of a pair alternating */
+} spava_schedule;
+
+/*
+ * Where the selection's second pass gets the float64 logits from
+ * (spava_shape.select_logits). Scores and indices are bitwise the same either way;
+ * the workspace size follows this field.
+ */
+typedef enum {
+  SPAVA_LOGITS_AUTO = 0,       /* keep the first pass's logits when one (block, KV head)
+                                  pair's take at most 512 MiB (G * w * n_b * 8 bytes),
+                                  in chunks of at most 4 GiB of logits; else recompute
+                                  (default)                                             */
+  SPAVA_LOGITS_RECOMPUTE = 1   /* always recompute them: less workspace, more time      */
+} spava_select_logits;
 
 /*
  * Problem shape and tensor layout.
@@ -96,6 +116,8 @@ typedef enum { SPAVA_BF16 = 0, SPAVA_F32 = 1 } spava_dtype;
  *   32-bit buffer offsets (63 token strides plus one row below 2^31 bytes).
  * Alignment (else SPAVA_ERR_ALIGN): tensor pointers 16-byte aligned; strides a
  * multiple of 8 elements (bf16) or 4 elements (f32).
+ * Options (else SPAVA_ERR_OPTION): schedule is a spava_schedule, select_logits a
+ * spava_select_logits. A zero-initialised struct selects the defaults.
  */
 typedef struct {
   int64_t seq_len;          /* N                                  */
@@ -111,12 +133,14 @@ typedef struct {
   int64_t q_stride_tok, q_stride_head;
   int64_t kv_stride_tok, kv_stride_head;
   int64_t o_stride_tok, o_stride_head;
+  int32_t schedule;         /* spava_schedule (0 = longest first) */
+  int32_t select_logits;    /* spava_select_logits (0 = auto)     */
 } spava_shape;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* spava_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (version 1 had no schedule / select_logits fields). */
 int spava_abi_version(void);
 
 /* Host-only check of a shape (no HIP call). SPAVA_OK or the error it would raise. */

@@ -29,27 +29,6 @@
 namespace spava {
 namespace {
 
-// Source token of prefix row r (anchor then passing rows of blocks 0, 1, ...) for KV
-// head g; -1 for padding rows and for indices outside the block's candidates.
-__device__ inline int64_t prefix_source(const Plan& p, const int32_t* idx, int g, int r) {
-  if (r < p.A) return r;
-  if (r >= p.Lmax) return -1;
-  int rr = r - p.A;
-  int j, t;
-  if (rr < p.l0) {
-    j = 0;
-    t = rr;
-  } else {
-    rr -= p.l0;
-    j = 1 + rr / p.l1;
-    t = rr % p.l1;
-  }
-  const int64_t src = idx[(static_cast<int64_t>(j) * p.Hkv + g) * p.l + t];
-  const int64_t s = static_cast<int64_t>(j) * p.nb;
-  const int64_t lo = j == 0 ? s + p.A : s;
-  return (src >= lo && src < s + p.nb) ? src : -1;
-}
-
 // Whole anchor tiles: prefix tiles [0, A / 64) hold anchor rows only.
 __host__ __device__ inline int anchor_tiles(const Plan& p) { return p.A / BN; }
 

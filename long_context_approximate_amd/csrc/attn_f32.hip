@@ -13,25 +13,6 @@ namespace {
 
 constexpr int BN = kKeyTile;
 
-__device__ inline int64_t prefix_source_f32(const Plan& p, const int32_t* idx, int g, int r) {
-  if (r < p.A) return r;
-  if (r >= p.Lmax) return -1;
-  int rr = r - p.A;
-  int j, t;
-  if (rr < p.l0) {
-    j = 0;
-    t = rr;
-  } else {
-    rr -= p.l0;
-    j = 1 + rr / p.l1;
-    t = rr % p.l1;
-  }
-  const int64_t src = idx[(static_cast<int64_t>(j) * p.Hkv + g) * p.l + t];
-  const int64_t s = static_cast<int64_t>(j) * p.nb;
-  const int64_t lo = j == 0 ? s + p.A : s;
-  return (src >= lo && src < s + p.nb) ? src : -1;
-}
-
 // Contiguous prefix copies Kpre/Vpre [Hkv][Lpad][D]; grid (Lpad/64, Hkv).
 template <int D>
 __global__ __launch_bounds__(256) void prep_f32_kernel(Plan p, const float* __restrict__ k,
@@ -44,7 +25,7 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(Plan p, const float* __re
   constexpr int CPR = D / 4;
   for (int c = threadIdx.x; c < BN * CPR; c += 256) {
     const int row = c / CPR, col = c % CPR;
-    const int64_t tok = prefix_source_f32(p, idx, g, r0 + row);
+    const int64_t tok = prefix_source(p, idx, g, r0 + row);
     float4 kk = make_float4(0, 0, 0, 0), vv = make_float4(0, 0, 0, 0);
     if (tok >= 0) {
       const int64_t off = tok * p.kvs_tok + g * p.kvs_head + col * 4;

@@ -54,6 +54,10 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   if (s->passing_len < 0) return SPAVA_ERR_SHAPE;
   if (s->window < 1 || s->window > nb) return SPAVA_ERR_SHAPE;
   if (!(s->sm_scale == s->sm_scale) || isinf(s->sm_scale)) return SPAVA_ERR_SHAPE;
+  if (s->schedule < SPAVA_SCHED_LONGEST_FIRST || s->schedule > SPAVA_SCHED_ZIGZAG)
+    return SPAVA_ERR_OPTION;
+  if (s->select_logits != SPAVA_LOGITS_AUTO && s->select_logits != SPAVA_LOGITS_RECOMPUTE)
+    return SPAVA_ERR_OPTION;
   const int64_t unit = s->dtype == SPAVA_BF16 ? 8 : 4;   // elements per 16 bytes
   const int64_t strides[6] = {s->q_stride_tok, s->q_stride_head, s->kv_stride_tok,
                               s->kv_stride_head, s->o_stride_tok, s->o_stride_head};
@@ -82,6 +86,8 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   p->kvs_head = s->kv_stride_head;
   p->os_tok = s->o_stride_tok;
   p->os_head = s->o_stride_head;
+  p->sched = s->schedule;
+  p->recompute_logits = s->select_logits == SPAVA_LOGITS_RECOMPUTE ? 1 : 0;
   // Rows each block passes: C_0 excludes the anchor, C_j (j >= 1) is the whole block.
   const int64_t l0 = p->H > 1 ? std::min<int64_t>(p->l, nb - p->A) : 0;
   const int64_t l1 = p->H > 2 ? std::min<int64_t>(p->l, nb) : 0;
@@ -96,8 +102,6 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   p->R = static_cast<int>(R);
   p->T = static_cast<int>(cdiv(nb, kQTile));
   p->loc_tiles = static_cast<int>(cdiv(nb, kKeyTile));
-  // SPAVA_SCHEDULE=lpt|natural|zigzag picks the attention dispatch order (default:
-  // longest first). Every order computes the same values; only timing differs.
   p->obs_query = 0;
   set_select_layout(p);
   // Every launch must fit a 32-bit work-item count and the int arithmetic of its
@@ -110,18 +114,13 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   const int64_t prep_groups = p->Lpad / kKeyTile + static_cast<int64_t>(p->H) * p->loc_tiles;
   if (!fits_launch({prep_groups, 256})) return SPAVA_ERR_SHAPE;           // gather
   if (!select_launches_fit(*p)) return SPAVA_ERR_SHAPE;
-  p->sched = kSchedLongestFirst;
-  if (const char* e = getenv("SPAVA_SCHEDULE")) {
-    if (strcmp(e, "natural") == 0) p->sched = kSchedNatural;
-    else if (strcmp(e, "zigzag") == 0) p->sched = kSchedZigZag;
-  }
   return SPAVA_OK;
 }
 
 // The selection's key split length (see kScoreSplitMin) and whether its score pass
-// reads stored logits. SPAVA_SELECT_LOGITS=recompute makes that pass recompute them
-// instead (less workspace, more time). Scores are bitwise the same either way: the
-// split length depends on the pair count of the whole call, not on the chunks.
+// reads stored logits (SPAVA_LOGITS_RECOMPUTE makes it recompute them: less
+// workspace, more time). Scores are bitwise the same either way: the split length
+// depends on the pair count of the whole call, not on the chunks.
 void set_select_layout(Plan* p) {
   const int64_t jg = static_cast<int64_t>(p->H > 1 ? p->H - 1 : 0) * p->Hkv;
   const int64_t row_tiles = cdiv(p->R, 32);
@@ -141,8 +140,7 @@ void set_select_layout(Plan* p) {
     }
   }
   p->KS = static_cast<int>(cdiv(p->nb, p->split_keys));
-  const char* e = getenv("SPAVA_SELECT_LOGITS");
-  const bool recompute = e && strcmp(e, "recompute") == 0;
+  const bool recompute = p->recompute_logits != 0;
   // A pair's stored logits: R rows of round_up(nb, 32) values (32-key tiles).
   // R * nbp * 8 <= kLogitPairBytes, tested without forming the (possibly huge) product.
   const int64_t nbp = round_up(p->nb, 32);
@@ -242,11 +240,12 @@ const char* spava_status_string(int status) {
     case SPAVA_ERR_WORKSPACE: return "SPAVA_ERR_WORKSPACE: workspace too small";
     case SPAVA_ERR_HIP: return "SPAVA_ERR_HIP: HIP runtime call or kernel launch failed";
     case SPAVA_ERR_DEVICE: return "SPAVA_ERR_DEVICE: current device is not gfx950";
+    case SPAVA_ERR_OPTION: return "SPAVA_ERR_OPTION: unknown schedule or select_logits value";
     default: return "SPAVA: unknown status";
   }
 }
 
-int spava_abi_version(void) { return 1; }
+int spava_abi_version(void) { return 2; }
 
 spava_status spava_validate_shape(const spava_shape* shape) {
   Plan p;

@@ -48,6 +48,7 @@ struct Plan {
   int sched;        // query-tile dispatch order (ScheduleMode); never changes results
   int obs_query;    // selection observers: 0 = last w queries of each block,
                     // 1 = the w rows of a query block (every key visible)
+  int recompute_logits;  // the caller asked for SPAVA_LOGITS_RECOMPUTE
   int store_logits; // 1: the score pass reads stored logits instead of recomputing
   int pair_chunk;   // (block, KV head) pairs per chunk when logits are stored
 };
@@ -55,8 +56,13 @@ struct Plan {
 // The selection's key splits and whether it stores its logits (after R is final).
 void set_select_layout(Plan* p);
 
-// Dispatch order of the (block, query tile) pairs of the attention grid.
-enum ScheduleMode { kSchedLongestFirst = 0, kSchedNatural = 1, kSchedZigZag = 2 };
+// Dispatch order of the (block, query tile) pairs of the attention grid (the values
+// of spava_schedule).
+enum ScheduleMode {
+  kSchedLongestFirst = SPAVA_SCHED_LONGEST_FIRST,
+  kSchedNatural = SPAVA_SCHED_NATURAL,
+  kSchedZigZag = SPAVA_SCHED_ZIGZAG
+};
 
 // Which keys an attention launch covers: all of them, or the split parts X (whole
 // anchor tiles + local keys) and Y (the rest of the prefix, merged with X).
@@ -65,6 +71,30 @@ enum AttnMode { kAttnFull = 0, kAttnPartX = 1, kAttnPartY = 2 };
 // Non-local prefix length of block h: anchor + passing rows of blocks 0..h-1.
 __host__ __device__ inline int prefix_len(const Plan& p, int h) {
   return h == 0 ? 0 : p.A + p.l0 + (h - 1) * p.l1;
+}
+
+// Source token of prefix row r for KV head g: the anchor rows [0, A), then the passing
+// rows of blocks 0, 1, ... in block order (explainer "APB-V: ...", Berechnung: the
+// anchor and the aggregated passing blocks). -1 for padding rows past Lmax and for an
+// index outside its block's candidates (block j's rows, minus the anchor for j = 0),
+// so a bad index reads as a zero row and never out of bounds.
+__device__ inline int64_t prefix_source(const Plan& p, const int32_t* idx, int g, int r) {
+  if (r < p.A) return r;
+  if (r >= p.Lmax) return -1;
+  int rr = r - p.A;
+  int j, t;
+  if (rr < p.l0) {
+    j = 0;
+    t = rr;
+  } else {
+    rr -= p.l0;
+    j = 1 + rr / p.l1;
+    t = rr % p.l1;
+  }
+  const int64_t src = idx[(static_cast<int64_t>(j) * p.Hkv + g) * p.l + t];
+  const int64_t s = static_cast<int64_t>(j) * p.nb;
+  const int64_t lo = j == 0 ? s + p.A : s;
+  return (src >= lo && src < s + p.nb) ? src : -1;
 }
 
 // Workspace carving (byte offsets, 256-byte aligned regions).

@@ -17,6 +17,17 @@ LIB_PATH = os.environ.get("SPAVA_LIB") or os.path.join(os.path.dirname(os.path.a
 SPAVA_BF16 = 0
 SPAVA_F32 = 1
 
+# spava_schedule: dispatch order of the attention's work items (timing only).
+SPAVA_SCHED_LONGEST_FIRST = 0
+SPAVA_SCHED_NATURAL = 1
+SPAVA_SCHED_ZIGZAG = 2
+SCHEDULES = {"lpt": SPAVA_SCHED_LONGEST_FIRST, "natural": SPAVA_SCHED_NATURAL,
+             "zigzag": SPAVA_SCHED_ZIGZAG}
+
+# spava_select_logits: whether the selection keeps or recomputes its float64 logits.
+SPAVA_LOGITS_AUTO = 0
+SPAVA_LOGITS_RECOMPUTE = 1
+
 # Every symbol include/spava.h declares.
 EXPORTS = (
     "spava_status_string",
@@ -55,6 +66,8 @@ class SpavaShape(ctypes.Structure):
         ("kv_stride_head", ctypes.c_int64),
         ("o_stride_tok", ctypes.c_int64),
         ("o_stride_head", ctypes.c_int64),
+        ("schedule", ctypes.c_int32),
+        ("select_logits", ctypes.c_int32),
     ]
 
 
@@ -122,19 +135,22 @@ def _check(status: int) -> None:
 
 
 def make_shape(seq_len, num_hosts, num_q_heads, num_kv_heads, head_dim, anchor_len,
-               passing_len, window, dtype=SPAVA_BF16, sm_scale=0.0, strides=None) -> SpavaShape:
+               passing_len, window, dtype=SPAVA_BF16, sm_scale=0.0, strides=None,
+               schedule=SPAVA_SCHED_LONGEST_FIRST, select_logits=SPAVA_LOGITS_AUTO) -> SpavaShape:
     """Shape with dense [N, heads, d] strides unless `strides` (6 ints) is given."""
     if strides is None:
         strides = (num_q_heads * head_dim, head_dim, num_kv_heads * head_dim, head_dim,
                    num_q_heads * head_dim, head_dim)
     return SpavaShape(seq_len, num_hosts, num_q_heads, num_kv_heads, head_dim, anchor_len,
-                      passing_len, window, dtype, sm_scale, *strides)
+                      passing_len, window, dtype, sm_scale, *strides, schedule, select_logits)
 
 
-def shape_from_config(cfg, sm_scale=0.0) -> SpavaShape:
+def shape_from_config(cfg, sm_scale=0.0, **options) -> SpavaShape:
+    """Dense-stride shape of a workload; `options` are schedule= / select_logits=."""
     dt = SPAVA_BF16 if cfg.dtype == "bf16" else SPAVA_F32
     return make_shape(cfg.seq_len, cfg.num_hosts, cfg.num_q_heads, cfg.num_kv_heads,
-                      cfg.head_dim, cfg.anchor_len, cfg.passing_len, cfg.window, dt, sm_scale)
+                      cfg.head_dim, cfg.anchor_len, cfg.passing_len, cfg.window, dt, sm_scale,
+                      **options)
 
 
 def validate_shape(shape: SpavaShape) -> int:
@@ -157,24 +173,122 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int | None:
+def _torch_stream(stream):
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    return stream if stream is not None else torch.cuda.current_stream()
 
 
-def _workspace(nbytes: int, device, workspace=None):
+def _stream(stream) -> int | None:
+    return _torch_stream(stream).cuda_stream
+
+
+# ----------------------------------------------------------- tensor validation
+#
+# The C ABI sees raw pointers only, so a tensor of the wrong dtype, device or size
+# would make the kernels read or write outside it. Every tensor is checked against
+# the shape here, before its pointer is taken: first dtype, sizes and strides of all
+# of them, then that all live on the same GPU.
+
+def _dtype_of(shape: SpavaShape):
+    import torch
+    if shape.dtype == SPAVA_BF16:
+        return torch.bfloat16
+    if shape.dtype == SPAVA_F32:
+        return torch.float32
+    raise ValueError(f"unknown dtype code {shape.dtype}")
+
+
+def _check_layout(name, t, dtype, sizes, strides):
+    """t has `dtype`; with sizes given, t.shape == sizes and, for every dimension longer
+    than 1, t.stride() == strides (strides None: contiguous)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if sizes is None:
+        return
+    if tuple(t.shape) != tuple(sizes):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(sizes)}")
+    if strides is None:
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        return
+    for dim, (n, st, want) in enumerate(zip(t.shape, t.stride(), strides)):
+        if n > 1 and st != want:
+            raise ValueError(f"{name}: stride {tuple(t.stride())} does not match the shape's "
+                             f"strides {tuple(strides)} (dimension {dim})")
+
+
+def _check_placement(named):
+    """Every tensor is a device tensor, all on the device of the first one."""
+    dev = None
+    for name, t in named:
+        if not t.is_cuda:
+            raise ValueError(f"{name}: must be a device (cuda) tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, expected {dev} like the other tensors")
+
+
+def _validate(shape: SpavaShape, n_rows=None, q=None, k=None, v=None, out=None, ctx_k=None,
+              ctx_v=None, passing_idx=None, scores_out=None, lse=None, lse_name="lse_out",
+              workspace=None, ws_bytes=0):
+    """Check the tensors of one call against `shape`. q/out are [n_rows, Hq, d] and k/v
+    [n_rows, Hkv, d] with the shape's strides (n_rows defaults to N); ctx_k/ctx_v are the
+    context's k/v ([N, Hkv, d]) of the query-block calls; passing_idx is int32
+    [max(H-1, 0), Hkv, l], scores_out float64 [max(H-1, 0), Hkv, N/H], lse float32
+    [Hq, n_rows], workspace uint8 with at least ws_bytes bytes; all contiguous but the
+    inputs and out."""
+    import torch
+    dt = _dtype_of(shape)
+    n = shape.seq_len if n_rows is None else n_rows
+    H, hq, hkv, d = shape.num_hosts, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    qs = (shape.q_stride_tok, shape.q_stride_head, 1)
+    kvs = (shape.kv_stride_tok, shape.kv_stride_head, 1)
+    os_ = (shape.o_stride_tok, shape.o_stride_head, 1)
+    nb = shape.seq_len // H if H > 0 else 0
+    items = [("q", q, dt, (n, hq, d), qs), ("k", k, dt, (n, hkv, d), kvs),
+             ("v", v, dt, (n, hkv, d), kvs), ("out", out, dt, (n, hq, d), os_),
+             ("k", ctx_k, dt, (shape.seq_len, hkv, d), kvs),
+             ("v", ctx_v, dt, (shape.seq_len, hkv, d), kvs),
+             ("passing_idx", passing_idx, torch.int32, (max(H - 1, 0), hkv, shape.passing_len),
+              None),
+             ("scores_out", scores_out, torch.float64, (max(H - 1, 0), hkv, nb), None),
+             (lse_name, lse, torch.float32, (hq, n), None)]
+    named = []
+    for name, t, dtype, sizes, strides in items:
+        if t is not None:
+            _check_layout(name, t, dtype, sizes, strides)
+            named.append((name, t))
+    if workspace is not None:
+        _check_layout("workspace", workspace, torch.uint8, None, None)
+        if not workspace.is_contiguous() or workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace: need a contiguous uint8 tensor of >= {ws_bytes} bytes, "
+                             f"got {workspace.numel()} bytes")
+        named.append(("workspace", workspace))
+    _check_placement(named)
+
+
+def _workspace(nbytes: int, device, workspace=None, stream=None):
+    """The caller's workspace (already validated), or a new one allocated on `stream`, so
+    the caching allocator only hands its memory to later work ordered after the kernels
+    that use it."""
     import torch
     if workspace is not None:
         return workspace
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(_torch_stream(stream)):
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def spava_select_passing(shape: SpavaShape, q, k, passing_idx, scores_out=None,
                          workspace=None, stream=None):
     """Write passing_idx (int32 [H-1, Hkv, l]) and optionally scores_out (f64 [H-1, Hkv, n_b])."""
     nbytes = spava_select_workspace_bytes(shape)
-    ws = _workspace(nbytes, q.device, workspace)
+    _validate(shape, q=q, k=k, passing_idx=passing_idx, scores_out=scores_out,
+              workspace=workspace, ws_bytes=nbytes)
+    ws = _workspace(nbytes, q.device, workspace, stream)
     _check(load().spava_select_passing(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(passing_idx),
                                        _ptr(scores_out), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(stream)))
@@ -185,7 +299,9 @@ def spava_approx_attn_fwd(shape: SpavaShape, q, k, v, passing_idx, out, lse_out=
                           workspace=None, stream=None):
     """Write out ([N, Hq, d]) and optionally lse_out (f32 [Hq, N])."""
     nbytes = spava_attn_workspace_bytes(shape)
-    ws = _workspace(nbytes, q.device, workspace)
+    _validate(shape, q=q, k=k, v=v, out=out, passing_idx=passing_idx, lse=lse_out,
+              workspace=workspace, ws_bytes=nbytes)
+    ws = _workspace(nbytes, q.device, workspace, stream)
     _check(load().spava_approx_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                         _ptr(passing_idx), _ptr(out), _ptr(lse_out), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)))
@@ -204,7 +320,9 @@ def spava_select_passing_query(shape: SpavaShape, q_qr, k, passing_idx, scores_o
     """Query-aware selection: observers are the rows of q_qr ([n_query, Hq, d])."""
     n_query = q_qr.shape[0]
     nbytes = spava_select_query_workspace_bytes(shape, n_query)
-    ws = _workspace(nbytes, q_qr.device, workspace)
+    _validate(shape, n_rows=n_query, q=q_qr, ctx_k=k, passing_idx=passing_idx,
+              scores_out=scores_out, workspace=workspace, ws_bytes=nbytes)
+    ws = _workspace(nbytes, q_qr.device, workspace, stream)
     _check(load().spava_select_passing_query(ctypes.byref(shape), n_query, _ptr(q_qr), _ptr(k),
                                              _ptr(passing_idx), _ptr(scores_out), _ptr(ws),
                                              ws.numel() * ws.element_size(), _stream(stream)))
@@ -222,7 +340,9 @@ def spava_query_attn_fwd(shape: SpavaShape, q_qr, k_qr, v_qr, k, v, out_qr, lse_
     """Write out_qr ([n_query, Hq, d]) and optionally lse_qr (f32 [Hq, n_query])."""
     n_query = q_qr.shape[0]
     nbytes = spava_query_workspace_bytes(shape, n_query)
-    ws = _workspace(nbytes, q_qr.device, workspace)
+    _validate(shape, n_rows=n_query, q=q_qr, k=k_qr, v=v_qr, out=out_qr, ctx_k=k, ctx_v=v,
+              lse=lse_qr, lse_name="lse_qr", workspace=workspace, ws_bytes=nbytes)
+    ws = _workspace(nbytes, q_qr.device, workspace, stream)
     _check(load().spava_query_attn_fwd(ctypes.byref(shape), n_query, _ptr(q_qr), _ptr(k_qr),
                                        _ptr(v_qr), _ptr(k), _ptr(v), _ptr(out_qr), _ptr(lse_qr),
                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
@@ -240,11 +360,16 @@ def spava_layer_overlap_fwd(shape: SpavaShape, q, k, v, passing_idx, out, lse_ou
     """Selection + attention of one layer, the selection on side_stream overlapped with
     the passing-independent attention on stream."""
     nbytes = spava_layer_overlap_workspace_bytes(shape)
-    ws = _workspace(nbytes, q.device, workspace)
-    main = _stream(stream)
-    side = side_stream.cuda_stream if side_stream is not None else None
-    if side is None:
+    if side_stream is None:
         raise ValueError("side_stream is required (a torch.cuda.Stream)")
+    _validate(shape, q=q, k=k, v=v, out=out, passing_idx=passing_idx, scores_out=scores_out,
+              lse=lse_out, workspace=workspace, ws_bytes=nbytes)
+    ws = _workspace(nbytes, q.device, workspace, stream)
+    # The side stream uses the workspace too: keep its memory from being handed out
+    # again before that stream's work is done.
+    ws.record_stream(side_stream)
+    main = _stream(stream)
+    side = side_stream.cuda_stream
     _check(load().spava_layer_overlap_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(passing_idx), _ptr(scores_out), _ptr(out),
                                           _ptr(lse_out), _ptr(ws), ws.numel() * ws.element_size(),
@@ -266,18 +391,23 @@ def device_tensors(x: dict, device="cuda"):
 
 
 def run_layer(shape: SpavaShape, q, k, v, want_scores=False, want_lse=True, stream=None):
-    """Selection then attention on device tensors; returns a dict of device tensors."""
+    """Selection then attention on device tensors; returns a dict of device tensors.
+
+    Outputs and workspaces are allocated on `stream` (default: the current stream), the
+    stream every kernel of the layer runs on."""
     import torch
     H, hkv, l = shape.num_hosts, shape.num_kv_heads, shape.passing_len
     nb = shape.seq_len // H
     dev = q.device
-    idx = torch.empty((max(H - 1, 0), hkv, l), dtype=torch.int32, device=dev)
-    scores = (torch.empty((max(H - 1, 0), hkv, nb), dtype=torch.float64, device=dev)
-              if want_scores else None)
-    spava_select_passing(shape, q, k, idx, scores, stream=stream)
-    out = torch.empty((shape.seq_len, shape.num_q_heads, shape.head_dim), dtype=q.dtype,
-                      device=dev)
-    lse = (torch.empty((shape.num_q_heads, shape.seq_len), dtype=torch.float32, device=dev)
-           if want_lse else None)
-    spava_approx_attn_fwd(shape, q, k, v, idx, out, lse, stream=stream)
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        idx = torch.empty((max(H - 1, 0), hkv, l), dtype=torch.int32, device=dev)
+        scores = (torch.empty((max(H - 1, 0), hkv, nb), dtype=torch.float64, device=dev)
+                  if want_scores else None)
+        out = torch.empty((shape.seq_len, shape.num_q_heads, shape.head_dim), dtype=q.dtype,
+                          device=dev)
+        lse = (torch.empty((shape.num_q_heads, shape.seq_len), dtype=torch.float32, device=dev)
+               if want_lse else None)
+    spava_select_passing(shape, q, k, idx, scores, stream=st)
+    spava_approx_attn_fwd(shape, q, k, v, idx, out, lse, stream=st)
     return {"idx": idx, "scores": scores, "out": out, "lse": lse}

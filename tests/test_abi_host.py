@@ -13,7 +13,7 @@ from long_context_approximate_amd import spava
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spava.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WS = 0, 1, 2, 3, 4, 5
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WS, ERR_OPTION = 0, 1, 2, 3, 4, 5, 8
 FAKE = 0x10000           # aligned non-null address; never dereferenced by these tests
 
 
@@ -38,9 +38,11 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_struct_layout_matches_header(lib):
-    assert ctypes.sizeof(spava.SpavaShape) == 96
+    assert ctypes.sizeof(spava.SpavaShape) == 104
     assert spava.SpavaShape.sm_scale.offset == 40
-    assert lib.spava_abi_version() == 1
+    assert spava.SpavaShape.schedule.offset == 96
+    assert spava.SpavaShape.select_logits.offset == 100
+    assert lib.spava_abi_version() == 2
 
 
 def _shape(**kw):
@@ -69,6 +71,12 @@ def _shape(**kw):
     ({"strides": (1024, 128, 17043520, 128, 1024, 128)}, ERR_SHAPE),
     ({"num_hosts": 1, "anchor_len": 0}, OK),
     ({"anchor_len": 1024, "passing_len": 0}, OK),
+    ({"schedule": 1}, OK),
+    ({"schedule": 2}, OK),
+    ({"schedule": 3}, ERR_OPTION),
+    ({"schedule": -1}, ERR_OPTION),
+    ({"select_logits": 1}, OK),
+    ({"select_logits": 2}, ERR_OPTION),
 ])
 def test_shape_validation(lib, kw, status):
     assert spava.validate_shape(_shape(**kw)) == status
@@ -149,14 +157,33 @@ def test_workspace_sizes(lib, kw):
     assert spava.spava_attn_workspace_bytes(sh) == attn
 
 
-def test_recompute_switch_drops_the_logit_workspace(lib, monkeypatch):
+def test_recompute_field_drops_the_logit_workspace(lib, monkeypatch):
+    # The size query follows the shape's select_logits field, and nothing else: the
+    # environment variables earlier versions read change nothing.
     sh = _shape()
     with_logits = spava.spava_select_workspace_bytes(sh)
-    monkeypatch.setenv("SPAVA_SELECT_LOGITS", "recompute")
-    without = spava.spava_select_workspace_bytes(sh)
+    without = spava.spava_select_workspace_bytes(_shape(select_logits=spava.SPAVA_LOGITS_RECOMPUTE))
     def r(b):
         return (b + 255) // 256 * 256
     assert with_logits - without == r(_logit_bytes(3 * 2, 4 * 32, 1024))
+    monkeypatch.setenv("SPAVA_SELECT_LOGITS", "recompute")
+    monkeypatch.setenv("SPAVA_SCHEDULE", "zigzag")
+    assert spava.spava_select_workspace_bytes(sh) == with_logits
+    # The query-aware selection sizes its logits the same way.
+    n = ctypes.c_size_t()
+    rq = _shape(select_logits=spava.SPAVA_LOGITS_RECOMPUTE)
+    assert lib.spava_select_query_workspace_bytes(ctypes.byref(sh), 100, ctypes.byref(n)) == OK
+    stored = n.value
+    assert lib.spava_select_query_workspace_bytes(ctypes.byref(rq), 100, ctypes.byref(n)) == OK
+    assert stored - n.value == r(_logit_bytes(3 * 2, 4 * 100, 1024))
+
+
+def test_schedule_field_leaves_workspace_sizes_alone(lib):
+    for mode in (1, 2):
+        assert spava.spava_attn_workspace_bytes(_shape(schedule=mode)) == \
+            spava.spava_attn_workspace_bytes(_shape())
+        assert spava.spava_select_workspace_bytes(_shape(schedule=mode)) == \
+            spava.spava_select_workspace_bytes(_shape())
 
 
 def test_calls_reject_bad_arguments_without_touching_the_gpu(lib):
@@ -254,7 +281,7 @@ def test_overlap_entry_workspace_and_validation(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         assert spava.status_string(code).startswith("SPAVA")
     assert "unknown" in spava.status_string(42)
 

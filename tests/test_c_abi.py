@@ -26,8 +26,13 @@ int main(void) {
   s.q_stride_tok = 28 * 128; s.q_stride_head = 128;
   s.kv_stride_tok = 4 * 128; s.kv_stride_head = 128;
   s.o_stride_tok = 28 * 128; s.o_stride_head = 128;
-  if (spava_abi_version() != 1) return 1;
-  if (spava_validate_shape(&s) != SPAVA_OK) return 2;
+  if (spava_abi_version() != 2) return 1;
+  if (spava_validate_shape(&s) != SPAVA_OK) return 2;       /* zeroed options: defaults */
+  s.schedule = SPAVA_SCHED_ZIGZAG; s.select_logits = SPAVA_LOGITS_RECOMPUTE;
+  if (spava_validate_shape(&s) != SPAVA_OK) return 10;
+  s.schedule = 7;
+  if (spava_validate_shape(&s) != SPAVA_ERR_OPTION) return 11;
+  s.schedule = SPAVA_SCHED_LONGEST_FIRST; s.select_logits = SPAVA_LOGITS_AUTO;
   if (spava_select_workspace_bytes(&s, &sel) != SPAVA_OK) return 3;
   if (spava_attn_workspace_bytes(&s, &attn) != SPAVA_OK) return 4;
   if (spava_layer_overlap_workspace_bytes(&s, &ovl) != SPAVA_OK) return 5;

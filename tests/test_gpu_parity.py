@@ -24,16 +24,18 @@ def _torch():
     return torch
 
 
-def _gpu_run(cfg, x=None, idx_override=None, strides=None):
+def _gpu_run(cfg, x=None, idx_override=None, strides=None, **options):
+    """Selection then attention through the C ABI; `options` are the shape's
+    schedule= / select_logits= fields."""
     torch = _torch()
     from long_context_approximate_amd import spava
     x = x if x is not None else make_inputs(cfg)
     dev = spava.device_tensors(x, "cuda")
-    shape = spava.shape_from_config(cfg)
+    shape = spava.shape_from_config(cfg, **options)
     if strides is not None:
         shape = spava.make_shape(cfg.seq_len, cfg.num_hosts, cfg.num_q_heads, cfg.num_kv_heads,
                                  cfg.head_dim, cfg.anchor_len, cfg.passing_len, cfg.window,
-                                 shape.dtype, 0.0, strides["shape"])
+                                 shape.dtype, 0.0, strides["shape"], **options)
         dev = strides["make"](dev)
     H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
     idx = torch.full((max(H - 1, 0), hkv, l), -7, dtype=torch.int32, device="cuda")
@@ -163,11 +165,11 @@ def test_strided_layout():
         vw = torch.zeros((n, 2 * hkv, d), dtype=torch.bfloat16, device="cuda")
         kw[:, :hkv] = dev["k"]
         vw[:, :hkv] = dev["v"]
-        return {"q": qw, "k": kw, "v": vw}
+        return {"q": qw[:, :, :d], "k": kw[:, :hkv], "v": vw[:, :hkv]}
 
     def out():
         holder["o"] = torch.zeros((n, hq, 2 * d), dtype=torch.bfloat16, device="cuda")
-        return holder["o"]
+        return holder["o"][:, :, :d]
 
     strides = {"shape": (hq * 2 * d, 2 * d, 2 * hkv * d, d, hq * 2 * d, 2 * d), "make": make,
                "out": out}
@@ -218,7 +220,7 @@ def test_large_kv_token_stride():
         vw = torch.zeros((n, slots, d), dtype=torch.bfloat16, device="cuda")
         kw[:, :hkv] = dev["k"]
         vw[:, :hkv] = dev["v"]
-        return {"q": dev["q"], "k": kw, "v": vw}
+        return {"q": dev["q"], "k": kw[:, :hkv], "v": vw[:, :hkv]}
 
     strides = {"shape": (hq * d, d, slots * d, d, hq * d, d), "make": make,
                "out": lambda: torch.full((n, hq, d), float("nan"), dtype=torch.bfloat16,
@@ -293,30 +295,32 @@ def _full_size_check(cfg):
     assert np.isfinite(got["out"]).all() and np.isfinite(got["lse"]).all()
 
 
-def test_schedules_give_identical_results(monkeypatch):
-    # The dispatch order (longest first, natural, ZigZag pairing) only changes timing.
+def test_schedules_give_identical_results():
+    # The dispatch order (longest first, natural, ZigZag pairing; the shape's schedule
+    # field) only changes timing.
+    from long_context_approximate_amd import spava
     cfg = small_config(name="sched", seq_len=4096, num_hosts=4, seed=26)
     x = make_inputs(cfg)
     results = {}
     for mode in ("lpt", "natural", "zigzag"):
-        monkeypatch.setenv("SPAVA_SCHEDULE", mode)
-        results[mode], _ = _gpu_run(cfg, x)
+        results[mode], _ = _gpu_run(cfg, x, schedule=spava.SCHEDULES[mode])
     for mode in ("natural", "zigzag"):
         for key in ("idx", "out", "lse"):
             assert np.array_equal(results[mode][key], results["lpt"][key]), (mode, key)
 
 
 @pytest.mark.parametrize("name", ["small", "h4_16k"])
-def test_stored_and_recomputed_logits_agree_bitwise(monkeypatch, name):
+def test_stored_and_recomputed_logits_agree_bitwise(name):
     # The score pass either reads the logits its first pass stored or recomputes them
-    # with the same products; both must give bitwise-equal scores and indices, and
-    # match the oracle.
+    # with the same products (the shape's select_logits field); both must give
+    # bitwise-equal scores and indices, and match the oracle.
+    from long_context_approximate_amd import spava
     cfg = small_config() if name == "small" else CONFIGS[name]
     x = make_inputs(cfg)
     results = {}
-    for mode in ("store", "recompute"):
-        monkeypatch.setenv("SPAVA_SELECT_LOGITS", mode)
-        results[mode], _ = _gpu_run(cfg, x)
+    for mode, code in (("store", spava.SPAVA_LOGITS_AUTO),
+                       ("recompute", spava.SPAVA_LOGITS_RECOMPUTE)):
+        results[mode], _ = _gpu_run(cfg, x, select_logits=code)
     for key in ("idx", "scores"):
         assert np.array_equal(results["store"][key], results["recompute"][key]), key
     sh = oracle.shape_of(cfg)
@@ -402,6 +406,30 @@ def test_layer_replays_from_a_hip_graph():
     r = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
     assert np.array_equal(got["idx"], r["idx"])
     _check_full(cfg, got, r)
+
+
+def test_layer_on_a_side_stream_while_the_current_stream_allocates():
+    # run_layer on a non-current stream allocates its outputs and workspaces on that
+    # stream. The current stream then allocates and fills memory before anything is
+    # synchronised: had the layer's workspaces come from the current stream's pool and
+    # been dropped, these fills could land in memory the layer's kernels still use.
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    cfg = small_config(name="side_stream", seq_len=3000, num_hosts=3, seed=73)
+    x = make_inputs(cfg)
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    res = spava.run_layer(shape, dev["q"], dev["k"], dev["v"], want_scores=True, stream=side)
+    junk = [torch.full((16 << 20,), 0xFF, dtype=torch.uint8, device="cuda") for _ in range(16)]
+    torch.cuda.synchronize()
+    del junk
+    got = {"idx": res["idx"].cpu().numpy(), "scores": res["scores"].cpu().numpy(),
+           "out": res["out"].float().cpu().numpy(), "lse": res["lse"].cpu().numpy()}
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    _check_selection(cfg, got, ref)
+    _check_full(cfg, got, ref)
 
 
 # ---------------------------------- overlapped layer (selection beside part X)
@@ -539,11 +567,11 @@ def test_query_block_video_workload():
 
 # ------------------------------------------------- query-aware selection variant
 
-def _gpu_query_select(cfg, x, q_qr):
+def _gpu_query_select(cfg, x, q_qr, **options):
     torch = _torch()
     from long_context_approximate_amd import spava
     dev = spava.device_tensors({"k": x["k"], "q_qr": q_qr}, "cuda")
-    shape = spava.shape_from_config(cfg)
+    shape = spava.shape_from_config(cfg, **options)
     H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
     idx = torch.full((max(H - 1, 0), hkv, l), -7, dtype=torch.int32, device="cuda")
     sc = torch.full((max(H - 1, 0), hkv, nb), -1.0, dtype=torch.float64, device="cuda")
@@ -573,14 +601,14 @@ def test_query_aware_selection_parity(cfg, nq):
     _check_selection(cfg, {"idx": idx, "scores": sc}, {"idx": ref_idx, "scores": ref_sc})
 
 
-def test_query_aware_selection_recompute_path(monkeypatch):
+def test_query_aware_selection_recompute_path():
+    from long_context_approximate_amd import spava
     cfg, nq = QSEL[2]
     x = make_inputs(cfg)
     qcfg = cfg.with_(seq_len=nq, num_hosts=1, anchor_len=0, window=1, seed=cfg.seed + 500)
     q_qr = make_inputs(qcfg)["q"]
     stored = _gpu_query_select(cfg, x, q_qr)
-    monkeypatch.setenv("SPAVA_SELECT_LOGITS", "recompute")
-    recomputed = _gpu_query_select(cfg, x, q_qr)
+    recomputed = _gpu_query_select(cfg, x, q_qr, select_logits=spava.SPAVA_LOGITS_RECOMPUTE)
     assert np.array_equal(stored[0], recomputed[0])
     assert np.array_equal(stored[1], recomputed[1])
 
