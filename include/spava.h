@@ -293,6 +293,36 @@ spava_status spava_layer_overlap_fwd(const spava_shape* shape, const void* q, co
                                      void* out, float* lse_out, void* workspace,
                                      size_t workspace_bytes, void* stream, void* side_stream);
 
+/*
+ * Allocation-free selection, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Computes exactly what spava_select_passing computes (same kernels; the float64
+ * logits are recomputed rather than stored, which gives bitwise the same scores and
+ * indices), but takes no workspace: its scratch (row statistics and, when scores_out
+ * is NULL, the scores) lives in a fixed array of SPAVA_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library, one per GPU, held until the process ends. The array's device
+ * address is looked up once per device on the first call there; nothing is allocated
+ * or freed, ever.
+ *
+ *   shape, q, k, passing_idx, scores_out   as in spava_select_passing
+ *                                          (shape->select_logits is ignored)
+ *   stream   hipStream_t (NULL = the default stream)
+ *
+ * SPAVA_ERR_WORKSPACE when the shape needs more scratch than the array holds (the
+ * selection workspace of the same shape with SPAVA_LOGITS_RECOMPUTE, which
+ * spava_select_workspace_bytes reports; 23.4 MiB for 262144 tokens in 16 blocks with
+ * 8 KV heads, G = 4 and w = 128). Nothing in the array needs to start at any value:
+ * every byte a call reads it first writes. All calls on one GPU share the array, so
+ * calls that overlap on one GPU (concurrent streams, or threads) race and must be
+ * ordered by the caller; calls on different GPUs do not interact.
+ */
+#define SPAVA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+spava_status spava_select_passing_noalloc(const spava_shape* shape, const void* q,
+                                          const void* k, int32_t* passing_idx,
+                                          double* scores_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

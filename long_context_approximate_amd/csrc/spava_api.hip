@@ -208,6 +208,30 @@ QueryWs query_ws_layout(const Plan& p, int64_t nq) {
   return w;
 }
 
+// Scratch of the allocation-free selection (spava_select_passing_noalloc): one copy
+// per GPU, held until the process ends. In host code `scratch` is only a stand-in for
+// the device array: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SPAVA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device (looked up on first use there).
+static spava_status scratch_address(char** out) {
+  static std::mutex mu;
+  static char* addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPAVA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return SPAVA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return SPAVA_ERR_HIP;
+    addr[dev] = static_cast<char*>(ptr);
+  }
+  *out = addr[dev];
+  return SPAVA_OK;
+}
+
 // gfx950 check, once per device ordinal.
 static spava_status check_device() {
   static std::mutex mu;
@@ -294,6 +318,35 @@ spava_status spava_select_passing(const spava_shape* shape, const void* q, const
   st = check_device();
   if (st != SPAVA_OK) return st;
   hipError_t e = launch_select(p, q, k, passing_idx, scores_out, static_cast<char*>(workspace),
+                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
+}
+
+spava_status spava_select_passing_noalloc(const spava_shape* shape, const void* q,
+                                          const void* k, int32_t* passing_idx,
+                                          double* scores_out, void* stream) {
+  if (!shape) return SPAVA_ERR_NULL;
+  // The same plan as spava_select_passing with the logits recomputed: the scratch then
+  // holds only the row statistics and the scores.
+  spava_shape s = *shape;
+  s.select_logits = SPAVA_LOGITS_RECOMPUTE;
+  Plan p;
+  spava_status st = make_plan(&s, &p);
+  if (st != SPAVA_OK) return st;
+  if (!q || !k) return SPAVA_ERR_NULL;
+  const bool any = p.H > 1 && p.l > 0;
+  if (any && !passing_idx) return SPAVA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k)) return SPAVA_ERR_ALIGN;
+  if (passing_idx && (reinterpret_cast<uintptr_t>(passing_idx) & 3u)) return SPAVA_ERR_ALIGN;
+  if (scores_out && (reinterpret_cast<uintptr_t>(scores_out) & 7u)) return SPAVA_ERR_ALIGN;
+  if (select_ws_layout(p).total > SPAVA_NOALLOC_SCRATCH_BYTES) return SPAVA_ERR_WORKSPACE;
+  if (p.H == 1 || (!any && !scores_out)) return SPAVA_OK;
+  st = check_device();
+  if (st != SPAVA_OK) return st;
+  char* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != SPAVA_OK) return st;
+  hipError_t e = launch_select(p, q, k, passing_idx, scores_out, ws,
                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPAVA_OK : SPAVA_ERR_HIP;
 }

@@ -43,7 +43,11 @@ EXPORTS = (
     "spava_select_passing_query",
     "spava_layer_overlap_workspace_bytes",
     "spava_layer_overlap_fwd",
+    "spava_select_passing_noalloc",
 )
+
+# Bytes of the library's fixed scratch array used by spava_select_passing_noalloc.
+SPAVA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SpavaShape(ctypes.Structure):
@@ -120,6 +124,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.spava_layer_overlap_workspace_bytes.restype = ctypes.c_int
     lib.spava_layer_overlap_fwd.argtypes = [shp, vp, vp, vp, i32p, f64p, vp, f32p, vp, sz, vp, vp]
     lib.spava_layer_overlap_fwd.restype = ctypes.c_int
+    lib.spava_select_passing_noalloc.argtypes = [shp, vp, vp, i32p, f64p, vp]
+    lib.spava_select_passing_noalloc.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -293,6 +299,16 @@ def spava_select_passing(shape: SpavaShape, q, k, passing_idx, scores_out=None,
                                        _ptr(scores_out), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(stream)))
     return ws
+
+
+def spava_select_passing_noalloc(shape: SpavaShape, q, k, passing_idx, scores_out=None,
+                                 stream=None):
+    """spava_select_passing without a workspace: the library's fixed per-GPU scratch
+    array is used instead. Calls on one GPU must not overlap."""
+    _validate(shape, q=q, k=k, passing_idx=passing_idx, scores_out=scores_out)
+    _check(load().spava_select_passing_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k),
+                                               _ptr(passing_idx), _ptr(scores_out),
+                                               _stream(stream)))
 
 
 def spava_approx_attn_fwd(shape: SpavaShape, q, k, v, passing_idx, out, lse_out=None,

@@ -280,6 +280,42 @@ def test_overlap_entry_workspace_and_validation(lib):
              None) == ERR_SHAPE
 
 
+def test_noalloc_selection_checks_before_touching_the_gpu(lib):
+    # The allocation-free selection validates like spava_select_passing and refuses a
+    # shape whose scratch (the recompute-mode selection workspace) exceeds the library's
+    # fixed 64 MiB array, all before any device call.
+    f = lib.spava_select_passing_noalloc
+    sh = _shape()
+    s = ctypes.byref(sh)
+    assert f(s, None, FAKE, FAKE, None, None) == ERR_NULL
+    assert f(s, FAKE, FAKE, None, None, None) == ERR_NULL
+    assert f(s, FAKE + 8, FAKE, FAKE, None, None) == ERR_ALIGN
+    assert f(s, FAKE, FAKE, FAKE + 2, None, None) == ERR_ALIGN
+    assert f(None, FAKE, FAKE, FAKE, None, None) == ERR_NULL
+    assert f(ctypes.byref(_shape(seq_len=4095)), FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    # 2^24 tokens in two blocks, 8 KV heads: 512 MiB of scores alone.
+    big = spava.make_shape(1 << 24, 2, 8, 8, 128, 0, 16, 1)
+    need = spava.spava_select_workspace_bytes(
+        spava.make_shape(1 << 24, 2, 8, 8, 128, 0, 16, 1,
+                         select_logits=spava.SPAVA_LOGITS_RECOMPUTE))
+    assert need > spava.SPAVA_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, None, None) == ERR_WS
+    # The largest named workload's scratch fits.
+    from long_context_approximate_amd.inputs import CONFIGS
+    for cfg in CONFIGS.values():
+        rs = spava.shape_from_config(cfg, select_logits=spava.SPAVA_LOGITS_RECOMPUTE)
+        assert spava.spava_select_workspace_bytes(rs) <= spava.SPAVA_NOALLOC_SCRATCH_BYTES
+    # One host: nothing to select, OK without any device call.
+    one = _shape(num_hosts=1, anchor_len=0)
+    assert f(ctypes.byref(one), FAKE, FAKE, None, None, None) == OK
+
+
+def test_noalloc_scratch_size_matches_the_header(lib):
+    text = open(HEADER).read()
+    assert "#define SPAVA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert spava.SPAVA_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_status_strings(lib):
     for code in range(9):
         assert spava.status_string(code).startswith("SPAVA")

@@ -65,6 +65,7 @@ DRIVER = textwrap.dedent(r"""
             lib.spava_query_attn_fwd(s, 16, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
                                      None)
             lib.spava_select_passing_query(s, 16, None, FAKE, FAKE, None, FAKE, 1 << 40, None)
+            lib.spava_select_passing_noalloc(s, None, FAKE, FAKE, None, None)
             count += 1
     for code in range(-1, 10):
         lib.spava_status_string(code)
