@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 METRIC = "approx-attn prefill tokens/s + TFLOP/s (% bf16 MFMA peak), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
 PEAK_CLOCK_GHZ = 2.4                # the clock the published peak assumes
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_h8_128k_pmc.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_{workload}_pmc.json")
 ATTN_SOURCES = [os.path.join(ROOT, "long_context_approximate_amd", "csrc", f)
                 for f in ("attn_bf16.hip", "attn_common.h")]
 
@@ -57,11 +57,12 @@ def attn_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def _profile_field(*keys):
-    """A number from the committed rocprofv3 counter summary, or None when the summary
-    is missing, lacks the field, or the attention source changed since it was taken."""
+def _profile_field(workload, *keys):
+    """A number from the committed rocprofv3 counter summary of this workload, or None
+    when the summary is missing, lacks the field, or the attention source changed since
+    it was taken."""
     try:
-        rec = json.load(open(PMC_SUMMARY))
+        rec = json.load(open(PMC_SUMMARY.format(workload=workload)))
         if rec.get("attn_sources_sha256") != attn_sources_sha256():
             return None
         for k in keys:
@@ -71,14 +72,14 @@ def _profile_field(*keys):
         return None
 
 
-def clock_from_profile():
+def clock_from_profile(workload):
     """Average shader clock (GHz) during the attention kernel (GRBM_GUI_ACTIVE run)."""
-    return _profile_field("attn_clock_ghz")
+    return _profile_field(workload, "attn_clock_ghz")
 
 
-def traffic_from_profile():
+def traffic_from_profile(workload):
     """HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE runs, calibrated)."""
-    return _profile_field("hbm_bytes_per_launch")
+    return _profile_field(workload, "hbm_bytes_per_launch")
 
 
 def score_flops(cfg) -> float:
@@ -383,11 +384,11 @@ def main():
         "t_attn_ms": t_attn * 1e3,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_from_profile()},
+                     "traffic": traffic_from_profile(cfg.name)},
     }
     rec["score_fp64_gflops"] = score_flops(cfg) / t_sel / 1e9
-    clock = clock_from_profile()
-    clock_dur = _profile_field("attn_clock_dur_us")
+    clock = clock_from_profile(cfg.name)
+    clock_dur = _profile_field(cfg.name, "attn_clock_dur_us")
     if clock is not None and clock_dur:
         # The published peak assumes 2.4 GHz; under sustained matrix load the chip runs
         # slower (and the clock differs from box to box), so the counter run's own
@@ -399,14 +400,14 @@ def main():
     # From the committed counter runs of this attention source (None when stale):
     # matrix-core busy fraction and HBM rate of the attention kernel, and the gather
     # (prep) kernel's duration.
-    busy = _profile_field("attn_mfma_busy_frac")
-    dur = _profile_field("attn_kernel", "dur_us")
-    hbm = traffic_from_profile()
+    busy = _profile_field(cfg.name, "attn_mfma_busy_frac")
+    dur = _profile_field(cfg.name, "attn_kernel", "dur_us")
+    hbm = traffic_from_profile(cfg.name)
     rec["profiled"] = {
         "attn_mfma_busy_frac": busy,
         "attn_hbm_gb_per_s": hbm / dur / 1e3 if hbm is not None and dur else None,
         "t_gather_ms": (lambda v: v / 1e3 if v is not None else None)(
-            _profile_field("prep_kernel", "dur_us")),
+            _profile_field(cfg.name, "prep_kernel", "dur_us")),
     }
     if not args.no_extras:
         rec["schedules_attn_ms"] = time_schedules(cfg, q, k, v, idx, out, lse, ws_attn, stream)

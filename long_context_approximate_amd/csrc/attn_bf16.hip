@@ -266,10 +266,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   }
 
   // ---- epilogue: normalise, round to bf16, write O and LSE
-  const float ltot = flash_rowsum<D>(f);
+  const float ltot = flash_rowsum<D>(f);       // float32 weights: the LSE
+  const float ltot_b = flash_rowsum_b<D>(f);   // bf16 weights: normalises O
   if (qi < e_h && mode == kAttnPartX && h >= 1) {
     // Part X of a block with a prefix: keep the normalised partial (O, log2-LSE).
-    const float inv = 1.f / ltot;
+    const float inv = 1.f / ltot_b;
     float* po = part_o + (qi * p.Hq + hq) * D;
 #pragma unroll
     for (int dm = 0; dm < C::DM; ++dm)
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   } else if (qi < e_h) {
     // Full output, or part Y merged with part X: O = (wx O_x + wy O_y) / (wx + wy) with
     // w = 2^LSE relative to the larger of the two LSEs.
-    float cx = 0.f, cy = 1.f / ltot, lse2 = f.mrun + log2f(ltot);
+    float cx = 0.f, cy = 1.f / ltot_b, lse2 = f.mrun + log2f(ltot);
     const float* po = nullptr;
     if (mode == kAttnPartY) {
       const float lx = part_lse[static_cast<int64_t>(hq) * p.N + qi];
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
       const float wx = exp2f(lx - mx), wy = ltot > 0.f ? exp2f(ly - mx) : 0.f;
       const float den = wx + wy;
       cx = wx / den;
-      cy = ltot > 0.f ? wy / (ltot * den) : 0.f;
+      cy = ltot > 0.f ? wy / (ltot_b * den) : 0.f;
       lse2 = mx + log2f(den);
       po = part_o + (qi * p.Hq + hq) * D;
     }

@@ -33,7 +33,9 @@ static_assert(kWaves * kWaveQ == kQTile, "query tile must match the plan");
 // raised to the tile maximum, O and the row sum rescaled and the tile recomputed. So
 // the per-tile maximum is never needed on the common path. The result is exact:
 // numerator and denominator share the reference. Raising the reference to a new
-// dominant logit keeps that key's weight at exactly 1, free of bf16 rounding in P.
+// dominant logit keeps that key's weight at exactly 1, free of bf16 rounding in P;
+// for a dominant key below that limit, O's normaliser sums the same bf16 weights the
+// product uses (Flash::lsum_b), so the key's rounding cancels.
 // kRefInit is finite so that masked scores (-inf) give p = 0 and never NaN.
 constexpr float kRefInit = -1.0e30f;
 constexpr float kSumLimit = 256.0f;
@@ -182,12 +184,17 @@ struct TileDma {
 __device__ inline void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Per-wave flash state for 32 queries: O^T accumulators, running reference max
-// (log2 units) and this lane's partial row sum (keys it holds; the partner lane
-// l ^ 32 holds the rest of the query's keys).
+// (log2 units) and this lane's partial row sums (keys it holds; the partner lane
+// l ^ 32 holds the rest of the query's keys): lsum of the float32 weights, which the
+// log-sum-exp uses, and lsum_b of the same weights rounded to bf16, exactly as they
+// enter the P V product, which normalises O. With one normaliser per side, numerator
+// and denominator carry the same rounding: a row dominated by one key whose weight
+// sits far from a power of two gets that key's v back, not v times its weight's bf16
+// rounding error (up to 2^-8, i.e. 0.018 for |v| = 4.5).
 template <int D>
 struct Flash {
   f32x16 o[Cfg<D>::DM];
-  float mrun, lsum;
+  float mrun, lsum, lsum_b;
   __device__ void init() {
 #pragma unroll
     for (int dm = 0; dm < Cfg<D>::DM; ++dm)
@@ -195,6 +202,7 @@ struct Flash {
       for (int r = 0; r < 16; ++r) o[dm][r] = 0.f;
     mrun = kRefInit;
     lsum = 0.f;
+    lsum_b = 0.f;
   }
 };
 
@@ -229,6 +237,27 @@ __device__ inline float exp_tile(const f32x16 (&s)[2], float ref, float c_log2, 
     }
   }
   return sum0 + sum1;
+}
+
+// Sum of this lane's 32 bf16 weights of a tile (v_dot2 against (1, 1): the products
+// are exact, two accumulation chains). Each dword is copied to a scalar before the
+// bit cast: a bit cast applied to a vector subscript directly lost the subscript
+// (every call read element 0).
+__device__ inline float bf16_tile_sum(const bf16x8 (&pf)[4]) {
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    const u32x4 w = __builtin_bit_cast(u32x4, pf[kc]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t word = w[e];
+      const bf16x2 pair = __builtin_bit_cast(bf16x2, word);
+      if (e & 1) s1 = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, s1, false);
+      else s0 = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, s0, false);
+    }
+  }
+  return s0 + s1;
 }
 
 // One 64-key tile for this wave's 32 queries: S^T = K Q^T, then, when `masked` (a
@@ -295,6 +324,7 @@ __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 
     const float alpha = __builtin_amdgcn_exp2f(f.mrun - mnew);
     f.mrun = mnew;
     f.lsum *= alpha;
+    f.lsum_b *= alpha;
 #pragma unroll
     for (int dm = 0; dm < C::DM; ++dm)
 #pragma unroll
@@ -302,6 +332,7 @@ __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 
     ps = exp_tile(s, mnew, c_log2, pf);
   }
   f.lsum += ps;
+  f.lsum_b += bf16_tile_sum(pf);
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -317,10 +348,15 @@ __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 
       f.o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc * C::DM + dm], pf[kc], f.o[dm], 0, 0, 0);
 }
 
-// Final row sum of this lane's query (both lanes of the pair hold the same value).
+// Final row sums of this lane's query (both lanes of the pair hold the same value):
+// of the float32 weights (for the log-sum-exp) and of the bf16 weights (normalises O).
 template <int D>
 __device__ inline float flash_rowsum(const Flash<D>& f) {
   return f.lsum + __shfl_xor(f.lsum, 32);
+}
+template <int D>
+__device__ inline float flash_rowsum_b(const Flash<D>& f) {
+  return f.lsum_b + __shfl_xor(f.lsum_b, 32);
 }
 
 // O[d] for this lane's query is f.o[dm][grp*4 + j] at d = dm*32 + 8*grp + 4*(l/32) + j.

@@ -117,9 +117,10 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
     wait_tile_loads();
     __syncthreads();
   }
-  const float ltot = flash_rowsum<D>(f);
+  const float ltot = flash_rowsum<D>(f);       // float32 weights: the LSE
+  const float ltot_b = flash_rowsum_b<D>(f);   // bf16 weights: normalises O
   if (qi < nq) {
-    const float inv = 1.f / ltot;
+    const float inv = 1.f / ltot_b;
     float* op = part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * D;
 #pragma unroll
     for (int dm = 0; dm < C::DM; ++dm)
