@@ -261,30 +261,27 @@ spava_status spava_layer_overlap_workspace_bytes(const spava_shape* shape, size_
 /*
  * One prefill layer with the selection overlapped ("Systemseitige Optimierungen" of
  * the explainer "APB-V: ...": passing blocks are transferred while attention computes;
- * on one GPU the transfer is the selection and gather, and the independent work is
- * the anchor and the local context).
+ * on one GPU the transfer is the selection, and the work that needs no passing rows is
+ * block 0's attention, whose queries see only their own causal keys).
  *
- * Computes exactly what spava_select_passing followed by spava_approx_attn_fwd compute,
- * with the attention split in two parts merged by log-sum-exp:
- *   on side_stream  the selection (passing_idx, scores_out), then the gather of the
- *                   passing rows;
- *   on stream       part X, every query against the whole 64-key tiles of the anchor
- *                   and its local keys (block 0 is complete after it), concurrently;
- *                   then, after the side stream, part Y: the rest of the prefix (the
- *                   passing rows, and the anchor's ragged last tile when A % 64 != 0),
- *                   merged with part X's (O, LSE) into out and lse_out.
- * Outputs match the two-call path to rounding (the merge changes the summation order;
- * indices and scores are the same).
+ * Computes exactly what spava_select_passing followed by spava_approx_attn_fwd
+ * compute, bitwise:
+ *   on side_stream  the selection (passing_idx, scores_out);
+ *   on stream       concurrently, the gather of the anchor tiles and of every block's
+ *                   local values and block 0's attention; then, after the side stream,
+ *                   the gather of the passing rows and the other blocks' attention.
  *
  *   q, k, v, passing_idx, scores_out, out, lse_out   as in the two calls above
  *   workspace     device, >= spava_layer_overlap_workspace_bytes bytes (the selection's
- *                 and the attention's workspaces plus part X's float32 (O, LSE),
- *                 N*Hq*d*4 + Hq*N*4 bytes)
+ *                 and the attention's workspaces)
  *   stream        hipStream_t the call is ordered on; every result is ready once it
  *                 reaches this point
  *   side_stream   a second hipStream_t (NULL = the default stream). It first waits for
- *                 work already enqueued on `stream`, so inputs produced there are safe.
- *                 Using the same stream twice is correct but overlaps nothing.
+ *                 work already enqueued on `stream`, so inputs produced there are safe;
+ *                 `stream` waits for it before the blocks that need passing rows. Using
+ *                 the same stream twice is correct but overlaps nothing.
+ * The call synchronises the two streams with two HIP events that the library creates
+ * once per calling thread and device and keeps for the life of the process.
  * bf16 only (SPAVA_ERR_DTYPE for f32). With H == 1 or l == 0 nothing needs selecting
  * and the plain attention runs on `stream`.
  */

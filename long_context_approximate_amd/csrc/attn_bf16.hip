@@ -18,12 +18,11 @@
 //              O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with float32 accumulators
 //              and an online softmax in float32 with exp2 and a folded scale.
 //
-// Split mode (the one-GPU form of the pages' overlap of passing-block transfers with
-// compute, "Systemseitige Optimierungen"): part X attends every query to the whole
-// anchor tiles and its local keys, which need no selection, and stores (O, LSE) per
-// query; part Y attends to the rest of the prefix (the passing rows, with the
-// anchor's ragged last tile) and merges with part X by log-sum-exp. X can run while
-// the selection runs on another stream.
+// A launch covers a range of blocks. The overlapped layer (the one-GPU form of the
+// pages' overlap of passing-block transfers with compute, "Systemseitige
+// Optimierungen") runs block 0, which sees no passing rows, while the selection runs
+// on another stream, and the other blocks after it; every query is computed exactly
+// as in a launch over all blocks.
 #include "attn_common.h"
 
 namespace spava {
@@ -32,17 +31,78 @@ namespace {
 // Whole anchor tiles: prefix tiles [0, A / 64) hold anchor rows only.
 __host__ __device__ inline int anchor_tiles(const Plan& p) { return p.A / BN; }
 
-// grid.x: prefix tiles [t0, t1), then (with_local) H*loc_tiles local V tiles;
-// grid.y: KV head.
+// Key tiles of work item `pair` (= block * T + query tile): the block's prefix tiles,
+// then its local tiles up to the last query of the tile.
+__device__ inline int pair_cost(const Plan& p, int pair) {
+  const int h = pair / p.T, t = pair % p.T;
+  const int loc = min(p.nb, (t + 1) * kQTile);
+  return (prefix_len(p, h) + BN - 1) / BN + (loc + BN - 1) / BN;
+}
+
+// order[rank] = pair for the pairs [pair0, pair0 + npairs) (whole blocks). Longest
+// first: pairs ranked by decreasing key-tile count, ties by pair index. Natural:
+// block-major. ZigZag: the range's blocks paired as (first + i, last - i), the pages'
+// host pairing, tiles of a pair alternating.
+// One 256-pair chunk of the ranking, by one workgroup of 256 threads (cost: LDS).
+__device__ inline void schedule_chunk(const Plan& p, int32_t* __restrict__ order, int pair0,
+                                      int npairs, int chunk, int* cost) {
+  const int P = npairs;
+  const int i = chunk * 256 + static_cast<int>(threadIdx.x);   // pair pair0 + i
+  const bool valid = i < P;
+  int rank = 0;
+  if (p.sched == kSchedNatural) {
+    rank = i;
+  } else if (p.sched == kSchedZigZag) {
+    const int nh = P / p.T;
+    const int h = i / p.T, t = i % p.T;
+    const int mirror = nh - 1 - h;
+    const int pr = min(h, mirror);
+    rank = (h == mirror) ? pr * 2 * p.T + t : pr * 2 * p.T + 2 * t + (h > mirror ? 1 : 0);
+  } else {
+    // Rank = number of pairs that come first (higher cost, or equal cost and lower
+    // index); the costs of each chunk of 256 pairs are computed once into LDS (slots
+    // past P hold -1, which never counts: costs are >= 0) and read 4 at a time.
+    const int ci = valid ? pair_cost(p, pair0 + i) : 0;
+    for (int j0 = 0; j0 < P; j0 += 256) {
+      __syncthreads();
+      const int jt = j0 + static_cast<int>(threadIdx.x);
+      cost[threadIdx.x] = jt < P ? pair_cost(p, pair0 + jt) : -1;
+      __syncthreads();
+      const int4* c4 = reinterpret_cast<const int4*>(cost);
+#pragma unroll 8
+      for (int q4 = 0; q4 < 64; ++q4) {
+        const int4 c = c4[q4];
+        const int jb = j0 + 4 * q4;
+        rank += (c.x > ci) || (c.x == ci && jb < i);
+        rank += (c.y > ci) || (c.y == ci && jb + 1 < i);
+        rank += (c.z > ci) || (c.z == ci && jb + 2 < i);
+        rank += (c.w > ci) || (c.w == ci && jb + 3 < i);
+      }
+    }
+  }
+  if (valid) order[rank] = pair0 + i;
+}
+
+// grid.x: prefix tiles [t0, t1), then (with_local) H*loc_tiles local V tiles, then
+// ceil(npairs / 256) workgroups that rank the work items of the attention launch that
+// follows (at grid.y == 0); grid.y: KV head.
 template <int D>
 __global__ __launch_bounds__(256) void prep_kernel(Plan p, const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v,
                                                    const int32_t* __restrict__ idx,
                                                    uint16_t* __restrict__ kpre,
                                                    uint16_t* __restrict__ vtpre,
-                                                   uint16_t* __restrict__ vtloc, int t0, int t1) {
+                                                   uint16_t* __restrict__ vtloc, int t0, int t1,
+                                                   int with_local, int32_t* __restrict__ order,
+                                                   int pair0, int npairs) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[BN][D + 8];
   __shared__ int64_t src_tok[BN];
+  __shared__ __attribute__((aligned(16))) int cost[256];
+  const int ngather = (t1 - t0) + (with_local ? p.H * p.loc_tiles : 0);
+  if (static_cast<int>(blockIdx.x) >= ngather) {
+    if (blockIdx.y == 0) schedule_chunk(p, order, pair0, npairs, blockIdx.x - ngather, cost);
+    return;
+  }
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int npre_tiles = p.Lpad / BN;
@@ -88,75 +148,13 @@ __global__ __launch_bounds__(256) void prep_kernel(Plan p, const uint16_t* __res
   store_vt_tile<D>(Vs, dst);
 }
 
-// Prefix tiles [pt0, pt1) and whether local tiles follow, for block h in a mode.
-struct TileRange {
-  int pt0, pt1, local;
-};
-__device__ inline TileRange tile_range(const Plan& p, int h, int mode) {
-  const int npre = (prefix_len(p, h) + BN - 1) / BN;
-  const int nax = h >= 1 ? anchor_tiles(p) : 0;
-  if (mode == kAttnPartX) return {0, nax, 1};
-  if (mode == kAttnPartY) return {nax, npre, 0};
-  return {0, npre, 1};
-}
-
-__device__ inline int pair_cost(const Plan& p, int pair, int mode) {
-  const int h = pair / p.T, t = pair % p.T;
-  const int loc = min(p.nb, (t + 1) * kQTile);
-  const TileRange tr = tile_range(p, h, mode);
-  return (tr.pt1 - tr.pt0) + (tr.local ? (loc + BN - 1) / BN : 0);
-}
-
-// order[rank] = pair (pair = block * T + query tile). Longest first: pairs ranked by
-// decreasing key-tile count, ties by pair index. Natural: block-major. ZigZag: blocks
-// paired as (p, H-1-p), the pages' host pairing, tiles of a pair alternating.
-__global__ __launch_bounds__(256) void schedule_kernel(Plan p, int32_t* __restrict__ order,
-                                                       int mode) {
-  __shared__ __attribute__((aligned(16))) int cost[256];
-  const int P = p.H * p.T;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const bool valid = i < P;
-  int rank = 0;
-  if (p.sched == kSchedNatural) {
-    rank = i;
-  } else if (p.sched == kSchedZigZag) {
-    const int h = i / p.T, t = i % p.T;
-    const int mirror = p.H - 1 - h;
-    const int pr = min(h, mirror);
-    rank = (h == mirror) ? pr * 2 * p.T + t : pr * 2 * p.T + 2 * t + (h > mirror ? 1 : 0);
-  } else {
-    // Rank = number of pairs that come first (higher cost, or equal cost and lower
-    // index); the costs of each chunk of 256 pairs are computed once into LDS (slots
-    // past P hold -1, which never counts: costs are >= 0) and read 4 at a time.
-    const int ci = valid ? pair_cost(p, i, mode) : 0;
-    for (int j0 = 0; j0 < P; j0 += 256) {
-      __syncthreads();
-      const int jt = j0 + static_cast<int>(threadIdx.x);
-      cost[threadIdx.x] = jt < P ? pair_cost(p, jt, mode) : -1;
-      __syncthreads();
-      const int4* c4 = reinterpret_cast<const int4*>(cost);
-#pragma unroll 8
-      for (int q4 = 0; q4 < 64; ++q4) {
-        const int4 c = c4[q4];
-        const int jb = j0 + 4 * q4;
-        rank += (c.x > ci) || (c.x == ci && jb < i);
-        rank += (c.y > ci) || (c.y == ci && jb + 1 < i);
-        rank += (c.z > ci) || (c.z == ci && jb + 2 < i);
-        rank += (c.w > ci) || (c.w == ci && jb + 3 < i);
-      }
-    }
-  }
-  if (valid) order[rank] = i;
-}
-
-template <int D, int MODE>
+// NG = (pairs in `order`) x Hkv work groups of G workgroups (one per query head).
+template <int D>
 __global__ __launch_bounds__(kThreads) void attn_kernel(
     Plan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kpre, const uint16_t* __restrict__ vtpre,
     const uint16_t* __restrict__ vtloc, const int32_t* __restrict__ order,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int NG, float c_log2,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
-  constexpr int mode = MODE;
+    uint16_t* __restrict__ out, float* __restrict__ lse, int NG, float c_log2) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
 
@@ -175,13 +173,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   const int64_t e_h = s_h + p.nb;
   const int64_t q0 = s_h + static_cast<int64_t>(t) * kQTile;
   const int64_t q_end = min(q0 + kQTile, e_h);
-  // Part Y of block 0 has nothing to do: part X wrote its final output.
-  if (mode == kAttnPartY && h == 0) return;
   const int L = prefix_len(p, h);
-  const int npre = (L + BN - 1) / BN;
-  const TileRange tr = tile_range(p, h, mode);
-  const int np = tr.pt1 - tr.pt0;
-  const int nloc = tr.local ? static_cast<int>((q_end - s_h + BN - 1) / BN) : 0;
+  const int np = (L + BN - 1) / BN;                                  // prefix tiles
+  const int nloc = static_cast<int>((q_end - s_h + BN - 1) / BN);   // local tiles
   const int ntiles = np + nloc;
 
   const int tid = threadIdx.x;
@@ -202,8 +196,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   dma.init(p.kvs_tok);
   // Per-workgroup tile bases and K ranges, so issuing a tile is a few scalar adds:
   // full local tiles share one range; only a block's last tile can be partial.
-  const uint16_t* kpre0 = kpre_g + static_cast<int64_t>(tr.pt0) * BN * D;
-  const uint16_t* vpre0 = vtpre_g + static_cast<int64_t>(tr.pt0) * D * BN;
+  const uint16_t* kpre0 = kpre_g;
+  const uint16_t* vpre0 = vtpre_g;
   const uint16_t* kloc0 = k_g + s_h * p.kvs_tok;
   const int64_t kloc_step = static_cast<int64_t>(BN) * p.kvs_tok;
   const int kbytes_pre = TileDma<D>::k_range(BN, D);
@@ -233,9 +227,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   // past the block end masks everything.
   const int64_t rel0 = qw0 - s_h;
   const int first_diag = rel0 >= BN - 1 ? static_cast<int>((rel0 - (BN - 1)) / BN) + 1 : 0;
-  const int it_diag = tr.local ? np + first_diag : ntiles;
-  const int it_edge =
-      ((L % BN) != 0 && npre - 1 >= tr.pt0 && npre - 1 < tr.pt1) ? npre - 1 - tr.pt0 : -1;
+  const int it_diag = np + first_diag;
+  const int it_edge = (L % BN) != 0 ? np - 1 : -1;
   const int qrel = static_cast<int>(qi - s_h);   // this lane's query inside the block
 
   if (ntiles > 0) issue_tile(0, smem);
@@ -252,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     const bool masked = diag || it == it_edge || !wave_active;
     int lim = BN - 1;
     if (masked) {
-      if (it == it_edge) lim = L - (tr.pt0 + it) * BN - 1;
+      if (it == it_edge) lim = L - it * BN - 1;
       if (diag) {
         const int rel = qrel - (it - np) * BN;      // integer select (no floating max)
         lim = rel < 0 ? -1 : rel;
@@ -268,47 +261,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   // ---- epilogue: normalise, round to bf16, write O and LSE
   const float ltot = flash_rowsum<D>(f);       // float32 weights: the LSE
   const float ltot_b = flash_rowsum_b<D>(f);   // bf16 weights: normalises O
-  if (qi < e_h && mode == kAttnPartX && h >= 1) {
-    // Part X of a block with a prefix: keep the normalised partial (O, log2-LSE).
-    const float inv = 1.f / ltot_b;
-    float* po = part_o + (qi * p.Hq + hq) * D;
-#pragma unroll
-    for (int dm = 0; dm < C::DM; ++dm)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        float4 v4;
-        v4.x = f.o[dm][grp * 4 + 0] * inv;
-        v4.y = f.o[dm][grp * 4 + 1] * inv;
-        v4.z = f.o[dm][grp * 4 + 2] * inv;
-        v4.w = f.o[dm][grp * 4 + 3] * inv;
-        *reinterpret_cast<float4*>(po + out_dim<D>(dm, grp, lh)) = v4;
-      }
-    if (lh == 0) part_lse[static_cast<int64_t>(hq) * p.N + qi] = f.mrun + log2f(ltot);
-  } else if (qi < e_h) {
-    // Full output, or part Y merged with part X: O = (wx O_x + wy O_y) / (wx + wy) with
-    // w = 2^LSE relative to the larger of the two LSEs.
-    float cx = 0.f, cy = 1.f / ltot_b, lse2 = f.mrun + log2f(ltot);
-    const float* po = nullptr;
-    if (mode == kAttnPartY) {
-      const float lx = part_lse[static_cast<int64_t>(hq) * p.N + qi];
-      const float ly = ltot > 0.f ? f.mrun + log2f(ltot) : -INFINITY;
-      const float mx = fmaxf(lx, ly);
-      const float wx = exp2f(lx - mx), wy = ltot > 0.f ? exp2f(ly - mx) : 0.f;
-      const float den = wx + wy;
-      cx = wx / den;
-      cy = ltot > 0.f ? wy / (ltot_b * den) : 0.f;
-      lse2 = mx + log2f(den);
-      po = part_o + (qi * p.Hq + hq) * D;
-    }
+  if (qi < e_h) {
+    const float cy = 1.f / ltot_b;
+    const float lse2 = f.mrun + log2f(ltot);
     uint16_t* op = out + qi * p.os_tok + hq * p.os_head;
 #pragma unroll
     for (int dm = 0; dm < C::DM; ++dm)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        float4 ox = {0.f, 0.f, 0.f, 0.f};
-        if (po) ox = *reinterpret_cast<const float4*>(po + out_dim<D>(dm, grp, lh));
-        f32x2 lo = {ox.x * cx + f.o[dm][grp * 4 + 0] * cy, ox.y * cx + f.o[dm][grp * 4 + 1] * cy};
-        f32x2 hi = {ox.z * cx + f.o[dm][grp * 4 + 2] * cy, ox.w * cx + f.o[dm][grp * 4 + 3] * cy};
+        f32x2 lo = {f.o[dm][grp * 4 + 0] * cy, f.o[dm][grp * 4 + 1] * cy};
+        f32x2 hi = {f.o[dm][grp * 4 + 2] * cy, f.o[dm][grp * 4 + 3] * cy};
         bf16x2 blo = __builtin_convertvector(lo, bf16x2);
         bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
         uint2 pk;
@@ -331,45 +293,40 @@ static AttnPtrs attn_ptrs(const Plan& p, char* ws) {
           reinterpret_cast<int32_t*>(ws + w.order2)};
 }
 
-// Gather prefix tiles [t0, t1) (and, with_local, every block's local V^T tiles).
+// Gather prefix tiles [t0, t1) (and, with_local, every block's local V^T tiles), and
+// rank the work items of blocks [h0, h1) into `order`, in one launch.
 template <int D>
 void launch_prep(const Plan& p, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                 const AttnPtrs& a, int t0, int t1, bool with_local, hipStream_t st) {
-  const unsigned gx = static_cast<unsigned>((t1 - t0) + (with_local ? p.H * p.loc_tiles : 0));
+                 const AttnPtrs& a, int t0, int t1, bool with_local, int32_t* order, int h0,
+                 int h1, hipStream_t st) {
+  const int P = (h1 - h0) * p.T;
+  const unsigned gx = static_cast<unsigned>((t1 - t0) + (with_local ? p.H * p.loc_tiles : 0) +
+                                            cdiv(P, 256));
   if (gx == 0) return;
   hipLaunchKernelGGL(prep_kernel<D>, dim3(gx, p.Hkv), dim3(256), 0, st, p, k, v, idx, a.kpre,
-                     a.vtpre, a.vtloc, t0, t1);
+                     a.vtpre, a.vtloc, t0, t1, with_local ? 1 : 0, order, h0 * p.T, P);
 }
 
-// Order the (block, query tile) pairs for `mode` and run the attention kernel.
+// Run the attention kernel over the work items of blocks [h0, h1), in `order`.
 template <int D>
-void launch_attn_mode(const Plan& p, const uint16_t* q, const uint16_t* k, const AttnPtrs& a,
-                      int32_t* order, uint16_t* out, float* lse, int mode, float* part_o,
-                      float* part_lse, hipStream_t st) {
-  const int P = p.H * p.T;
-  hipLaunchKernelGGL(schedule_kernel, dim3(static_cast<unsigned>(cdiv(P, 256))), dim3(256), 0, st,
-                     p, order, mode);
+void launch_attn_blocks(const Plan& p, const uint16_t* q, const uint16_t* k, const AttnPtrs& a,
+                        int32_t* order, uint16_t* out, float* lse, int h0, int h1,
+                        hipStream_t st) {
+  const int P = (h1 - h0) * p.T;
+  if (P <= 0) return;
   const int NG = P * p.Hkv;
   const int64_t grid = round_up(NG, 8) * p.G;
   const float c_log2 = static_cast<float>(p.scale * 1.4426950408889634);
-  const dim3 gd(static_cast<unsigned>(grid));
-  if (mode == kAttnPartX)
-    hipLaunchKernelGGL((attn_kernel<D, kAttnPartX>), gd, dim3(kThreads), 0, st, p, q, k, a.kpre,
-                       a.vtpre, a.vtloc, order, out, lse, NG, c_log2, part_o, part_lse);
-  else if (mode == kAttnPartY)
-    hipLaunchKernelGGL((attn_kernel<D, kAttnPartY>), gd, dim3(kThreads), 0, st, p, q, k, a.kpre,
-                       a.vtpre, a.vtloc, order, out, lse, NG, c_log2, part_o, part_lse);
-  else
-    hipLaunchKernelGGL((attn_kernel<D, kAttnFull>), gd, dim3(kThreads), 0, st, p, q, k, a.kpre,
-                       a.vtpre, a.vtloc, order, out, lse, NG, c_log2, part_o, part_lse);
+  hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p,
+                     q, k, a.kpre, a.vtpre, a.vtloc, order, out, lse, NG, c_log2);
 }
 
 template <int D>
 hipError_t launch_d(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* idx, uint16_t* out, float* lse, char* ws, hipStream_t st) {
   const AttnPtrs a = attn_ptrs(p, ws);
-  launch_prep<D>(p, k, v, idx, a, 0, p.Lpad / BN, true, st);
-  launch_attn_mode<D>(p, q, k, a, a.order, out, lse, kAttnFull, nullptr, nullptr, st);
+  launch_prep<D>(p, k, v, idx, a, 0, p.Lpad / BN, true, a.order, 0, p.H, st);
+  launch_attn_blocks<D>(p, q, k, a, a.order, out, lse, 0, p.H, st);
   return hipGetLastError();
 }
 
@@ -385,45 +342,42 @@ hipError_t launch_attn_bf16(const Plan& p, const void* q, const void* k, const v
   return launch_d<64>(p, qq, kk, vv, idx, oo, lse, ws, st);
 }
 
-hipError_t launch_attn_bf16_part_x(const Plan& p, const void* q, const void* k, const void* v,
-                                   void* out, float* lse, char* ws, float* part_o,
-                                   float* part_lse, hipStream_t st) {
+hipError_t launch_attn_bf16_block0(const Plan& p, const void* q, const void* k, const void* v,
+                                   void* out, float* lse, char* ws, hipStream_t st) {
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(out);
   const AttnPtrs a = attn_ptrs(p, ws);
+  // The whole-anchor prefix tiles and every block's local V^T tiles need no indices.
   if (p.D == 128) {
-    launch_prep<128>(p, kk, vv, nullptr, a, 0, anchor_tiles(p), true, st);
-    launch_attn_mode<128>(p, qq, kk, a, a.order, oo, lse, kAttnPartX, part_o, part_lse, st);
+    launch_prep<128>(p, kk, vv, nullptr, a, 0, anchor_tiles(p), true, a.order, 0, 1, st);
+    launch_attn_blocks<128>(p, qq, kk, a, a.order, oo, lse, 0, 1, st);
   } else {
-    launch_prep<64>(p, kk, vv, nullptr, a, 0, anchor_tiles(p), true, st);
-    launch_attn_mode<64>(p, qq, kk, a, a.order, oo, lse, kAttnPartX, part_o, part_lse, st);
+    launch_prep<64>(p, kk, vv, nullptr, a, 0, anchor_tiles(p), true, a.order, 0, 1, st);
+    launch_attn_blocks<64>(p, qq, kk, a, a.order, oo, lse, 0, 1, st);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16_gather_passing(const Plan& p, const void* k, const void* v,
-                                           const int32_t* idx, char* ws, hipStream_t st) {
-  auto kk = static_cast<const uint16_t*>(k);
-  auto vv = static_cast<const uint16_t*>(v);
-  const AttnPtrs a = attn_ptrs(p, ws);
-  if (p.D == 128) launch_prep<128>(p, kk, vv, idx, a, anchor_tiles(p), p.Lpad / BN, false, st);
-  else launch_prep<64>(p, kk, vv, idx, a, anchor_tiles(p), p.Lpad / BN, false, st);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_bf16_part_y(const Plan& p, const void* q, const void* k, void* out,
-                                   float* lse, char* ws, float* part_o, float* part_lse,
-                                   hipStream_t st) {
+hipError_t launch_attn_bf16_rest(const Plan& p, const void* q, const void* k, const void* v,
+                                 const int32_t* idx, void* out, float* lse, char* ws,
+                                 hipStream_t st) {
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
+  auto vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(out);
   const AttnPtrs a = attn_ptrs(p, ws);
-  if (p.D == 128)
-    launch_attn_mode<128>(p, qq, kk, a, a.order2, oo, lse, kAttnPartY, part_o, part_lse, st);
-  else
-    launch_attn_mode<64>(p, qq, kk, a, a.order2, oo, lse, kAttnPartY, part_o, part_lse, st);
+  // The prefix tiles from the anchor's ragged last tile on hold passing rows.
+  if (p.D == 128) {
+    launch_prep<128>(p, kk, vv, idx, a, anchor_tiles(p), p.Lpad / BN, false, a.order2, 1, p.H,
+                     st);
+    launch_attn_blocks<128>(p, qq, kk, a, a.order2, oo, lse, 1, p.H, st);
+  } else {
+    launch_prep<64>(p, kk, vv, idx, a, anchor_tiles(p), p.Lpad / BN, false, a.order2, 1, p.H,
+                    st);
+    launch_attn_blocks<64>(p, qq, kk, a, a.order2, oo, lse, 1, p.H, st);
+  }
   return hipGetLastError();
 }
 

@@ -111,8 +111,10 @@ static spava_status make_plan(const spava_shape* s, Plan* p) {
   const int64_t attn_groups = round_up(static_cast<int64_t>(p->H) * p->T * p->Hkv, 8);
   if (!fits_launch({attn_groups, p->G, 512})) return SPAVA_ERR_SHAPE;    // attention
   if (!fits_launch({p->H, p->loc_tiles})) return SPAVA_ERR_SHAPE;
-  const int64_t prep_groups = p->Lpad / kKeyTile + static_cast<int64_t>(p->H) * p->loc_tiles;
-  if (!fits_launch({prep_groups, 256})) return SPAVA_ERR_SHAPE;           // gather
+  // The gather launch also carries the workgroups that rank the attention's work items.
+  const int64_t prep_groups = p->Lpad / kKeyTile + static_cast<int64_t>(p->H) * p->loc_tiles +
+                              cdiv(static_cast<int64_t>(p->H) * p->T, 256);
+  if (!fits_launch({prep_groups, p->Hkv, 256})) return SPAVA_ERR_SHAPE;   // gather
   if (!select_launches_fit(*p)) return SPAVA_ERR_SHAPE;
   return SPAVA_OK;
 }
@@ -188,8 +190,6 @@ OverlapWs overlap_ws_layout(const Plan& p) {
   size_t cur = 0;
   w.select = region(cur, select_ws_layout(p).total);
   w.attn = region(cur, attn_ws_layout(p).total);
-  w.part_o = region(cur, static_cast<size_t>(p.N) * p.Hq * p.D * sizeof(float));
-  w.part_lse = region(cur, static_cast<size_t>(p.Hq) * p.N * sizeof(float));
   w.total = cur;
   return w;
 }
@@ -512,33 +512,35 @@ spava_status spava_layer_overlap_fwd(const spava_shape* shape, const void* q, co
                ? SPAVA_OK
                : SPAVA_ERR_HIP;
   }
-  float* part_o = reinterpret_cast<float*>(ws + w.part_o);
-  float* part_lse = reinterpret_cast<float*>(ws + w.part_lse);
-  hipEvent_t inputs_ready = nullptr, passing_ready = nullptr;
-  if (hipEventCreateWithFlags(&inputs_ready, hipEventDisableTiming) != hipSuccess)
-    return SPAVA_ERR_HIP;
-  if (hipEventCreateWithFlags(&passing_ready, hipEventDisableTiming) != hipSuccess) {
-    (void)hipEventDestroy(inputs_ready);
-    return SPAVA_ERR_HIP;
-  }
+  // Two events per thread and device, created on first use and kept: this entry
+  // records and waits on them within one call, so reusing them across calls (in
+  // stream order) is safe, and concurrent callers on other threads have their own.
+  struct CallEvents {
+    hipEvent_t ev[64][2];
+  };
+  thread_local CallEvents tev{};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPAVA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return SPAVA_ERR_DEVICE;
+  for (int i = 0; i < 2; ++i)
+    if (tev.ev[dev][i] == nullptr &&
+        hipEventCreateWithFlags(&tev.ev[dev][i], hipEventDisableTiming) != hipSuccess) {
+      tev.ev[dev][i] = nullptr;
+      return SPAVA_ERR_HIP;
+    }
+  hipEvent_t inputs_ready = tev.ev[dev][0], passing_ready = tev.ev[dev][1];
   bool ok = true;
-  // Side stream: selection, then the gather of the passing rows. It starts once the
-  // main stream has reached this call (the inputs are ready there).
+  // Side stream: the selection, once the main stream has reached this call (the inputs
+  // are ready there).
   ok = ok && hipEventRecord(inputs_ready, main_st) == hipSuccess;
   ok = ok && hipStreamWaitEvent(side_st, inputs_ready, 0) == hipSuccess;
   ok = ok && launch_select(p, q, k, passing_idx, scores_out, ws + w.select, side_st) == hipSuccess;
-  ok = ok && launch_attn_bf16_gather_passing(p, k, v, passing_idx, ws + w.attn, side_st) ==
-                 hipSuccess;
   ok = ok && hipEventRecord(passing_ready, side_st) == hipSuccess;
-  // Main stream: part X meanwhile, then part Y once the passing rows are gathered.
-  ok = ok && launch_attn_bf16_part_x(p, q, k, v, out, lse_out, ws + w.attn, part_o, part_lse,
-                                     main_st) == hipSuccess;
+  // Main stream: block 0 meanwhile (no passing rows), then the other blocks.
+  ok = ok && launch_attn_bf16_block0(p, q, k, v, out, lse_out, ws + w.attn, main_st) == hipSuccess;
   ok = ok && hipStreamWaitEvent(main_st, passing_ready, 0) == hipSuccess;
-  ok = ok && launch_attn_bf16_part_y(p, q, k, out, lse_out, ws + w.attn, part_o, part_lse,
-                                     main_st) == hipSuccess;
-  // Destroying a recorded event is allowed; its resources go once it completes.
-  (void)hipEventDestroy(inputs_ready);
-  (void)hipEventDestroy(passing_ready);
+  ok = ok && launch_attn_bf16_rest(p, q, k, v, passing_idx, out, lse_out, ws + w.attn, main_st) ==
+                 hipSuccess;
   return ok ? SPAVA_OK : SPAVA_ERR_HIP;
 }
 

@@ -64,10 +64,6 @@ enum ScheduleMode {
   kSchedZigZag = SPAVA_SCHED_ZIGZAG
 };
 
-// Which keys an attention launch covers: all of them, or the split parts X (whole
-// anchor tiles + local keys) and Y (the rest of the prefix, merged with X).
-enum AttnMode { kAttnFull = 0, kAttnPartX = 1, kAttnPartY = 2 };
-
 // Non-local prefix length of block h: anchor + passing rows of blocks 0..h-1.
 __host__ __device__ inline int prefix_len(const Plan& p, int h) {
   return h == 0 ? 0 : p.A + p.l0 + (h - 1) * p.l1;
@@ -105,9 +101,9 @@ struct AttnWs {
   size_t kpre, vpre, vtloc, order, order2, total;
 };
 
-// Workspace of the overlapped layer: selection, attention, and part X's (O, LSE).
+// Workspace of the overlapped layer: the selection's and the attention's.
 struct OverlapWs {
-  size_t select, attn, part_o, part_lse, total;
+  size_t select, attn, total;
 };
 
 struct QueryWs {
@@ -126,16 +122,15 @@ hipError_t launch_select(const Plan& p, const void* q, const void* k, int32_t* i
 hipError_t launch_attn_bf16(const Plan& p, const void* q, const void* k, const void* v,
                             const int32_t* idx, void* out, float* lse, char* ws,
                             hipStream_t st);
-// Split attention (bf16): part X needs no passing rows; the passing gather needs the
-// selection; part Y needs both and merges into out/lse.
-hipError_t launch_attn_bf16_part_x(const Plan& p, const void* q, const void* k, const void* v,
-                                   void* out, float* lse, char* ws, float* part_o,
-                                   float* part_lse, hipStream_t st);
-hipError_t launch_attn_bf16_gather_passing(const Plan& p, const void* k, const void* v,
-                                           const int32_t* idx, char* ws, hipStream_t st);
-hipError_t launch_attn_bf16_part_y(const Plan& p, const void* q, const void* k, void* out,
-                                   float* lse, char* ws, float* part_o, float* part_lse,
-                                   hipStream_t st);
+// The bf16 attention in two launches (the overlapped layer): block 0, which sees no
+// passing rows (also gathers the anchor tiles and every block's local V^T), then the
+// other blocks (gathers the passing rows first). Together they compute exactly what
+// launch_attn_bf16 computes.
+hipError_t launch_attn_bf16_block0(const Plan& p, const void* q, const void* k, const void* v,
+                                   void* out, float* lse, char* ws, hipStream_t st);
+hipError_t launch_attn_bf16_rest(const Plan& p, const void* q, const void* k, const void* v,
+                                 const int32_t* idx, void* out, float* lse, char* ws,
+                                 hipStream_t st);
 hipError_t launch_attn_f32(const Plan& p, const void* q, const void* k, const void* v,
                            const int32_t* idx, void* out, float* lse, char* ws,
                            hipStream_t st);

@@ -77,4 +77,4 @@ def test_c_program_links_and_runs_host_calls(cc, tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
     sel, attn, ovl, qry = (int(v) for v in run.stdout.split()[:4])
-    assert sel > 3_000_000_000 and attn > 0 and ovl > sel + attn and qry > 0
+    assert sel > 3_000_000_000 and attn > 0 and ovl >= sel + attn and qry > 0
