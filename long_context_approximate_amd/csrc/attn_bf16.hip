@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     const uint16_t* __restrict__ vtloc, const int32_t* __restrict__ order,
     uint16_t* __restrict__ out, float* __restrict__ lse, int NG, float c_log2) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[3 * C::STAGE];
 
   // Work item: XCD-aware mapping so the G heads of one KV group run back to back
   // on one XCD (consecutive workgroup ids are spread round-robin over 8 XCDs).
@@ -231,12 +231,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   const int it_edge = (L % BN) != 0 ? np - 1 : -1;
   const int qrel = static_cast<int>(qi - s_h);   // this lane's query inside the block
 
+  // Three LDS stages, tiles loaded one iteration ahead of their use: while tile it is
+  // computed, tile it+1 is complete (its first K fragments go into registers during
+  // tile it's P V) and tile it+2 is in flight into the stage tile it-1 used.
   if (ntiles > 0) issue_tile(0, smem);
+  if (ntiles > 1) issue_tile(1, smem + C::STAGE);
   wait_tile_loads();
   __syncthreads();
-
+  KHead<D> kh;
+  kh.read(smem);
+  int st = 0;   // stage of tile it
   for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) issue_tile(it + 1, smem + ((it + 1) & 1) * C::STAGE);
+    const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+    if (it + 2 < ntiles) issue_tile(it + 2, smem + st2 * C::STAGE);
     // Last visible key of a masked tile: the prefix length in the partial prefix
     // tile, the causal diagonal in a local tile. Tiles past this wave's queries are
     // processed fully masked (lim = -1) rather than branched around, which keeps the
@@ -252,10 +259,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
       }
       if (!wave_active) lim = -1;
     }
-    const char* ks = smem + (it & 1) * C::STAGE;
-    attend_tile<D>(ks, ks + C::KBYTES, qf, f, masked, lim, c_log2);
-    wait_tile_loads();
+    attend_tile<D>(kh, smem + st * C::STAGE, it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr,
+                   qf, f, masked, lim, c_log2);
+    wait_tile_loads();   // tile it+2, which the next iteration's P V reads K from
     __syncthreads();
+    st = st1;
   }
 
   // ---- epilogue: normalise, round to bf16, write O and LSE

@@ -260,26 +260,52 @@ __device__ inline float bf16_tile_sum(const bf16x8 (&pf)[4]) {
   return s0 + s1;
 }
 
-// One 64-key tile for this wave's 32 queries: S^T = K Q^T, then, when `masked` (a
-// wave-uniform flag), hide keys kk > lim (kk = key index inside the tile; lim >= 63
-// hides nothing), online softmax in the log2 domain against the running reference,
-// then O^T += V^T P^T. LDS fragments are read in batches ahead of their products (all
-// K fragments first; V^T fragments in two halves), so each batch is in flight while
-// earlier work runs.
+// K fragments held ahead of a tile step: those of the first kKHead head-dim steps
+// (kKHead of DK, 32-row key blocks both). The loop reads them for tile t+1 from LDS
+// during the second half of tile t's P V, so the products of tile t+1 start without
+// waiting for LDS; the remaining DK - kKHead steps are read at the start of the step.
+// (All DK steps ahead would need 32 more registers than two waves per SIMD allow.)
 template <int D>
-__device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 (&qf)[Cfg<D>::DK],
-                                   Flash<D>& f, bool masked, int lim, float c_log2) {
+struct KHead {
+  static constexpr int kSteps = Cfg<D>::DK < 4 ? Cfg<D>::DK : 4;
+  bf16x8 f[2 * kSteps];
+  __device__ void read(const char* ks) {
+    using C = Cfg<D>;
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int dk = 0; dk < kSteps; ++dk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        f[dk * 2 + kb] = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + lr) * C::KROWB +
+                                                         (dk * 16 + lh * 8) * 2);
+  }
+};
+
+// One 64-key tile (K rows at ks, V^T at ks + KBYTES) for this wave's 32 queries:
+// S^T = K Q^T, then, when `masked` (a wave-uniform flag), hide keys kk > lim (kk = key
+// index inside the tile; lim >= 63 hides nothing), online softmax in the log2 domain
+// against the running reference, then O^T += V^T P^T. kh holds this tile's first K
+// fragments on entry; when ks_next is not null it holds the next tile's on return
+// (read during the second half of P V). LDS fragments are read in batches ahead of
+// their products (the rest of K first; V^T in two halves), so each batch is in flight
+// while earlier work runs.
+template <int D>
+__device__ inline void attend_tile(KHead<D>& kh, const char* ks, const char* ks_next,
+                                   const bf16x8 (&qf)[Cfg<D>::DK], Flash<D>& f, bool masked,
+                                   int lim, float c_log2) {
   using C = Cfg<D>;
+  constexpr int KH = KHead<D>::kSteps;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
-  bf16x8 kf[2 * C::DK];
+  const char* vs = ks + C::KBYTES;
+  bf16x8 kr[2 * (C::DK - KH) + 1];
 #pragma unroll
-  for (int dk = 0; dk < C::DK; ++dk)
+  for (int dk = KH; dk < C::DK; ++dk)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      kf[dk * 2 + kb] = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + lr) * C::KROWB +
-                                                        (dk * 16 + lh * 8) * 2);
-  __builtin_amdgcn_sched_barrier(0);
+      kr[(dk - KH) * 2 + kb] = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + lr) * C::KROWB +
+                                                               (dk * 16 + lh * 8) * 2);
   f32x16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -289,7 +315,8 @@ __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 
   for (int dk = 0; dk < C::DK; ++dk)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk * 2 + kb], qf[dk], s[kb], 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          dk < KH ? kh.f[dk * 2 + kb] : kr[(dk - KH) * 2 + kb], qf[dk], s[kb], 0, 0, 0);
   // V^T fragments of key chunks 0-1 now (in flight during the softmax), of chunks 2-3
   // once the first half of the products is issued.
   bf16x8 vf[4 * C::DM];
@@ -340,6 +367,7 @@ __device__ inline void attend_tile(const char* ks, const char* vs, const bf16x8 
       f.o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc * C::DM + dm], pf[kc], f.o[dm], 0, 0, 0);
   read_v(2);
   read_v(3);
+  if (ks_next != nullptr) kh.read(ks_next);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kc = 2; kc < 4; ++kc)

@@ -112,7 +112,9 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
       if (self && qi - key0 < lim) lim = qi - key0;
       const char* ks = smem + (it & 1) * C::STAGE;
       const int lim32 = lim < BN - 1 ? static_cast<int>(lim) : BN - 1;
-      attend_tile<D>(ks, ks + C::KBYTES, qf, f, __any(lim32 < BN - 1) != 0, lim32, c_log2);
+      KHead<D> kh;
+      kh.read(ks);
+      attend_tile<D>(kh, ks, nullptr, qf, f, __any(lim32 < BN - 1) != 0, lim32, c_log2);
     }
     wait_tile_loads();
     __syncthreads();
