@@ -64,3 +64,48 @@ def test_full_size_128k_then_16k():
     for name in ("h8_128k", "h4_16k"):
         cfg = CONFIGS[name]
         _compare(cfg, make_inputs(cfg))
+
+
+def test_float32_and_d64_shapes():
+    # The float32 selection kernels and head dimension 64 through the same scratch.
+    for cfg in (small_config(name="na_f32", dtype="f32", seq_len=1200, num_hosts=4, seed=85),
+                small_config(name="na_d64", head_dim=64, seq_len=2048, num_hosts=4,
+                             num_q_heads=8, num_kv_heads=2, anchor_len=64, passing_len=128,
+                             window=64, seed=86)):
+        x = make_inputs(cfg)
+        idx, _ = _compare(cfg, x)
+        ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"], attention=False)
+        assert np.array_equal(idx, ref["idx"])
+
+
+def test_captured_in_a_hip_graph_and_replayed():
+    # The reason for the entry: it can be captured (nothing is allocated). Every replay,
+    # with eager work and synchronisation in between, must give the eager result.
+    import torch
+    from long_context_approximate_amd import spava
+    cfg = small_config(name="na_graph", seq_len=3000, num_hosts=3, seed=87)
+    x = make_inputs(cfg)
+    dev = spava.device_tensors({"q": x["q"], "k": x["k"]}, "cuda")
+    shape = spava.shape_from_config(cfg)
+    H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
+    idx = torch.empty((H - 1, hkv, l), dtype=torch.int32, device="cuda")
+    sc = torch.empty((H - 1, hkv, nb), dtype=torch.float64, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        spava.spava_select_passing_noalloc(shape, dev["q"], dev["k"], idx, sc)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = (idx.clone(), sc.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        spava.spava_select_passing_noalloc(shape, dev["q"], dev["k"], idx, sc)
+    for rep in range(3):
+        idx.zero_()
+        sc.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0]) and torch.equal(sc, ref[1]), f"replay {rep} differs"
+    r = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"], attention=False)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"])
