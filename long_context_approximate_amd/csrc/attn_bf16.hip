@@ -266,28 +266,43 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     st = st1;
   }
 
-  // ---- epilogue: normalise, round to bf16, write O and LSE
+  // ---- epilogue: normalise, round to bf16, write O and LSE. Each wave stages its 32
+  // output rows in LDS (no wave reads a stage after the loop's last barrier) and then
+  // stores whole rows, 16 bytes per lane: stored straight from the accumulator layout,
+  // every store instruction would write 16 bytes into each of 32 rows (16K tokens:
+  // the attention call 3% slower).
   const float ltot = flash_rowsum<D>(f);       // float32 weights: the LSE
   const float ltot_b = flash_rowsum_b<D>(f);   // bf16 weights: normalises O
-  if (qi < e_h) {
-    const float cy = 1.f / ltot_b;
-    const float lse2 = f.mrun + log2f(ltot);
-    uint16_t* op = out + qi * p.os_tok + hq * p.os_head;
+  constexpr int ORB = 2 * D + 16;              // bytes per staged row (padded)
+  static_assert(kWaves * kWaveQ * ORB <= 3 * C::STAGE, "staged rows must fit the stages");
+  char* ob = smem + w * (kWaveQ * ORB);
+  const float cy = 1.f / ltot_b;
 #pragma unroll
-    for (int dm = 0; dm < C::DM; ++dm)
+  for (int dm = 0; dm < C::DM; ++dm)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        f32x2 lo = {f.o[dm][grp * 4 + 0] * cy, f.o[dm][grp * 4 + 1] * cy};
-        f32x2 hi = {f.o[dm][grp * 4 + 2] * cy, f.o[dm][grp * 4 + 3] * cy};
-        bf16x2 blo = __builtin_convertvector(lo, bf16x2);
-        bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
-        uint2 pk;
-        pk.x = __builtin_bit_cast(uint32_t, blo);
-        pk.y = __builtin_bit_cast(uint32_t, bhi);
-        *reinterpret_cast<uint2*>(op + out_dim<D>(dm, grp, lh)) = pk;
-      }
-    if (lse && lh == 0) lse[static_cast<int64_t>(hq) * p.N + qi] = lse2 * 0.69314718055994531f;
+    for (int grp = 0; grp < 4; ++grp) {
+      f32x2 lo = {f.o[dm][grp * 4 + 0] * cy, f.o[dm][grp * 4 + 1] * cy};
+      f32x2 hi = {f.o[dm][grp * 4 + 2] * cy, f.o[dm][grp * 4 + 3] * cy};
+      bf16x2 blo = __builtin_convertvector(lo, bf16x2);
+      bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
+      uint2 pk;
+      pk.x = __builtin_bit_cast(uint32_t, blo);
+      pk.y = __builtin_bit_cast(uint32_t, bhi);
+      *reinterpret_cast<uint2*>(ob + lr * ORB + out_dim<D>(dm, grp, lh) * 2) = pk;
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's rows are in LDS
+  __builtin_amdgcn_wave_barrier();
+  constexpr int LPR = 2 * D / 16;       // lanes per row
+  constexpr int RPS = 64 / LPR;         // rows per store
+#pragma unroll
+  for (int j = 0; j < kWaveQ / RPS; ++j) {
+    const int row = j * RPS + lane / LPR, c16 = lane % LPR;
+    const u32x4 v4 = *reinterpret_cast<const u32x4*>(ob + row * ORB + c16 * 16);
+    const int64_t qrow = qw0 + row;
+    if (qrow < e_h) *reinterpret_cast<u32x4*>(out + qrow * p.os_tok + hq * p.os_head + c16 * 8) = v4;
   }
+  if (lse && lh == 0 && qi < e_h)
+    lse[static_cast<int64_t>(hq) * p.N + qi] = (f.mrun + log2f(ltot)) * 0.69314718055994531f;
 }
 
 struct AttnPtrs {
