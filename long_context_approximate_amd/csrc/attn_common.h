@@ -220,7 +220,8 @@ __device__ inline void load_q(const uint16_t* qp, bool ok, bf16x8 (&qf)[Cfg<D>::
 // p = exp2(c*s - ref) of this lane's 32 scores, packed to bf16 in the P^T operand
 // order; returns the lane's partial sum of the float32 values.
 __device__ inline float exp_tile(const f32x16 (&s)[2], float ref, float c_log2, bf16x8 (&pf)[4]) {
-  float sum0 = 0.f, sum1 = 0.f;
+  // Two chains, each started from its first pair (p >= 0, so this equals 0 + pair).
+  float sum0, sum1;
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
     const int kb = kc >> 1, half = kc & 1;
@@ -229,8 +230,9 @@ __device__ inline float exp_tile(const f32x16 (&s)[2], float ref, float c_log2, 
       const int r = half * 8 + 2 * e2;
       f32x2 two = {__builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -ref)),
                    __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c_log2, -ref))};
-      if (kc & 1) sum1 += two[0] + two[1];
-      else sum0 += two[0] + two[1];
+      const float pr = two[0] + two[1];
+      if (kc & 1) sum1 = (kc == 1 && e2 == 0) ? pr : sum1 + pr;
+      else sum0 = (kc == 0 && e2 == 0) ? pr : sum0 + pr;
       const bf16x2 cv = __builtin_convertvector(two, bf16x2);
       pf[kc][2 * e2] = cv[0];
       pf[kc][2 * e2 + 1] = cv[1];
