@@ -262,10 +262,10 @@ __device__ inline float bf16_tile_sum(const bf16x8 (&pf)[4]) {
   return s0 + s1;
 }
 
-// K fragments held ahead of a tile step: those of the first kKHead head-dim steps
-// (kKHead of DK, 32-row key blocks both). The loop reads them for tile t+1 from LDS
+// K fragments held ahead of a tile step: those of the first kSteps head-dim steps
+// (kSteps of DK, both 32-row key blocks). The loop reads them for tile t+1 from LDS
 // during the second half of tile t's P V, so the products of tile t+1 start without
-// waiting for LDS; the remaining DK - kKHead steps are read at the start of the step.
+// waiting for LDS; the remaining DK - kSteps steps are read at the start of the step.
 // (All DK steps ahead would need 32 more registers than two waves per SIMD allow.)
 template <int D>
 struct KHead {
