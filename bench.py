@@ -50,10 +50,15 @@ def attn_flops(cfg) -> float:
 
 
 def attn_sources_sha256() -> str:
-    """Hash of the attention kernel's source files (the counters are tied to it)."""
+    """Hash of the attention kernel's source code (the counters are tied to it): the
+    files with `//` comments, trailing blanks and empty lines removed, so that editing
+    a comment does not mark the profiles stale."""
     h = hashlib.sha256()
     for path in ATTN_SOURCES:
-        h.update(open(path, "rb").read())
+        for line in open(path, encoding="utf-8").read().splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
