@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
     const uint16_t* __restrict__ vtctx, const uint16_t* __restrict__ vtq,
     float* __restrict__ part_o, float* __restrict__ part_lse, float c_log2) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[3 * C::STAGE];
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int gs = (slot / p.G) * 8 + xcd;
@@ -99,25 +99,33 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
   Flash<D> f;
   f.init();
 
+  // The main attention's three-stage ring: while tile it is computed, tile it+1 is
+  // complete (its first K fragments are read during tile it's P V) and tile it+2 is in
+  // flight. A wave that skips a tile (past its queries in the query block, or no
+  // queries at all) skips every later one, so it never needs the prefetched fragments.
   if (ntiles > 0) issue_tile(0, smem);
+  if (ntiles > 1) issue_tile(1, smem + C::STAGE);
   wait_tile_loads();
   __syncthreads();
+  KHead<D> kh;
+  if (ntiles > 0) kh.read(smem);
+  int st = 0;   // stage of tile it
   for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) issue_tile(it + 1, smem + ((it + 1) & 1) * C::STAGE);
+    const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+    if (it + 2 < ntiles) issue_tile(it + 2, smem + st2 * C::STAGE);
     const int64_t key0 = static_cast<int64_t>(it) * BN;
     const bool skip = !wave_active || (self && key0 > qw_last);
     if (!skip) {
       // Hide keys past the segment end; in the query block also keys after the query.
       int64_t lim = nkeys - key0 - 1;
       if (self && qi - key0 < lim) lim = qi - key0;
-      const char* ks = smem + (it & 1) * C::STAGE;
       const int lim32 = lim < BN - 1 ? static_cast<int>(lim) : BN - 1;
-      KHead<D> kh;
-      kh.read(ks);
-      attend_tile<D>(kh, ks, nullptr, qf, f, __any(lim32 < BN - 1) != 0, lim32, c_log2);
+      attend_tile<D>(kh, smem + st * C::STAGE, it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr,
+                     qf, f, __any(lim32 < BN - 1) != 0, lim32, c_log2);
     }
-    wait_tile_loads();
+    wait_tile_loads();   // tile it+2
     __syncthreads();
+    st = st1;
   }
   const float ltot = flash_rowsum<D>(f);       // float32 weights: the LSE
   const float ltot_b = flash_rowsum_b<D>(f);   // bf16 weights: normalises O
