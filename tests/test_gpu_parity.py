@@ -458,6 +458,50 @@ def test_layer_replays_from_a_hip_graph():
     _check_full(cfg, got, r)
 
 
+def test_overlapped_layer_replays_from_a_hip_graph():
+    # The overlapped layer forks the selection onto a side stream and joins it back with
+    # two events, so a capture of the main stream takes in the side stream's work too.
+    # Replays (eager work and synchronisation in between) must match the eager call
+    # bitwise, and the eager call must match the oracle.
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    cfg = small_config(name="graph_overlap", seq_len=3000, num_hosts=3, seed=74)
+    x = make_inputs(cfg)
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    H, hkv, l = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len
+    ws = torch.empty(spava.spava_layer_overlap_workspace_bytes(shape), dtype=torch.uint8,
+                     device="cuda")
+    idx = torch.empty((H - 1, hkv, l), dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.seq_len, cfg.num_q_heads, cfg.head_dim), dtype=dev["q"].dtype,
+                      device="cuda")
+    lse = torch.empty((cfg.num_q_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+
+    def layer():
+        spava.spava_layer_overlap_fwd(shape, dev["q"], dev["k"], dev["v"], idx, out, lse,
+                                      workspace=ws, side_stream=side)
+
+    layer()                                       # eager reference (and the events' creation)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (idx, out, lse)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    for rep in range(3):
+        for t in (idx, out, lse):
+            t.zero_()                             # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((idx, out, lse), ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+    got = {"idx": idx.cpu().numpy(), "out": out.float().cpu().numpy(), "lse": lse.cpu().numpy()}
+    r = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    assert np.array_equal(got["idx"], r["idx"])
+    _check_full(cfg, got, r)
+
+
 def test_layer_on_a_side_stream_while_the_current_stream_allocates():
     # run_layer on a non-current stream allocates its outputs and workspaces on that
     # stream. The current stream then allocates and fills memory before anything is
