@@ -221,6 +221,17 @@ def _time_call(fn, stream, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def without_lse_timing(cfg, shape, q, k, v, idx, out, ws, stream, t_attn, reps=5):
+    """The attention call with lse_out = NULL (O only): the kernel variant without the
+    float32 weight sum. The step above writes the LSE; this is the same call for a
+    caller that does not need it."""
+    from long_context_approximate_amd import spava
+    ms = _time_call(lambda: spava.spava_approx_attn_fwd(shape, q, k, v, idx, out, None, ws, stream),
+                    stream, reps)
+    return {"attn_ms": ms, "tflops": attn_flops(cfg) / ms / 1e9,
+            "speedup_vs_with_lse": t_attn * 1e3 / ms}
+
+
 def time_schedules(cfg, q, k, v, idx, out, lse, ws, stream, reps=3):
     """Attention-call time under each dispatch order (the shape's schedule field; same
     results, different timing)."""
@@ -416,6 +427,8 @@ def main():
     }
     if not args.no_extras:
         rec["schedules_attn_ms"] = time_schedules(cfg, q, k, v, idx, out, lse, ws_attn, stream)
+        rec["attn_without_lse"] = without_lse_timing(cfg, shape, q, k, v, idx, out, ws_attn,
+                                                     stream, t_attn)
         rec["dense_causal"] = dense_baseline(cfg, q, k, v, stream, t_step)
         rec["query_block"] = query_block_timing(cfg, shape, k, v, stream)
         rec["overlap"] = overlap_timing(shape, q, k, v, idx, out, lse, stream, t_step)

@@ -197,7 +197,9 @@ spava_status spava_select_passing(const spava_shape* shape, const void* q, const
  *                block j's candidates; an entry outside them is read as a zero row
  *                (never out of bounds).
  *   out          device [N, Hq, d] via o_* strides, dtype per shape (written)
- *   lse_out      device float32 [Hq, N] (written) or NULL
+ *   lse_out      device float32 [Hq, N] (written) or NULL. With NULL (bf16) the
+ *                kernel skips the float32 weight sum (3-5% faster); O is the same up
+ *                to rounding (the running reference may be raised at another tile).
  *   workspace    device, >= spava_attn_workspace_bytes bytes (contents scratch)
  */
 spava_status spava_approx_attn_fwd(const spava_shape* shape, const void* q, const void* k,

@@ -149,7 +149,9 @@ __global__ __launch_bounds__(256) void prep_kernel(Plan p, const uint16_t* __res
 }
 
 // NG = (pairs in `order`) x Hkv work groups of G workgroups (one per query head).
-template <int D>
+// LSE: write the log-sum-exp (the caller asked for it), which adds the float32 sum of
+// the weights to every tile step.
+template <int D, bool LSE>
 __global__ __launch_bounds__(kThreads) void attn_kernel(
     Plan p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kpre, const uint16_t* __restrict__ vtpre,
@@ -259,8 +261,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
       }
       if (!wave_active) lim = -1;
     }
-    attend_tile<D>(kh, smem + st * C::STAGE, it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr,
-                   qf, f, masked, lim, c_log2);
+    attend_tile<D, LSE>(kh, smem + st * C::STAGE,
+                        it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr, qf, f, masked, lim,
+                        c_log2);
     wait_tile_loads();   // tile it+2, which the next iteration's P V reads K from
     __syncthreads();
     st = st1;
@@ -271,7 +274,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   // stores whole rows, 16 bytes per lane: stored straight from the accumulator layout,
   // every store instruction would write 16 bytes into each of 32 rows (16K tokens:
   // the attention call 3% slower).
-  const float ltot = flash_rowsum<D>(f);       // float32 weights: the LSE
   const float ltot_b = flash_rowsum_b<D>(f);   // bf16 weights: normalises O
   constexpr int ORB = 2 * D + 16;              // bytes per staged row (padded)
   static_assert(kWaves * kWaveQ * ORB <= 3 * C::STAGE, "staged rows must fit the stages");
@@ -301,8 +303,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     const int64_t qrow = qw0 + row;
     if (qrow < e_h) *reinterpret_cast<u32x4*>(out + qrow * p.os_tok + hq * p.os_head + c16 * 8) = v4;
   }
-  if (lse && lh == 0 && qi < e_h)
-    lse[static_cast<int64_t>(hq) * p.N + qi] = (f.mrun + log2f(ltot)) * 0.69314718055994531f;
+  if (LSE) {
+    const float ltot = flash_rowsum<D>(f);     // float32 weights: the LSE
+    if (lh == 0 && qi < e_h)
+      lse[static_cast<int64_t>(hq) * p.N + qi] = (f.mrun + log2f(ltot)) * 0.69314718055994531f;
+  }
 }
 
 struct AttnPtrs {
@@ -340,8 +345,12 @@ void launch_attn_blocks(const Plan& p, const uint16_t* q, const uint16_t* k, con
   const int NG = P * p.Hkv;
   const int64_t grid = round_up(NG, 8) * p.G;
   const float c_log2 = static_cast<float>(p.scale * 1.4426950408889634);
-  hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p,
-                     q, k, a.kpre, a.vtpre, a.vtloc, order, out, lse, NG, c_log2);
+  if (lse)
+    hipLaunchKernelGGL((attn_kernel<D, true>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       0, st, p, q, k, a.kpre, a.vtpre, a.vtloc, order, out, lse, NG, c_log2);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, false>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       0, st, p, q, k, a.kpre, a.vtpre, a.vtloc, order, out, lse, NG, c_log2);
 }
 
 template <int D>

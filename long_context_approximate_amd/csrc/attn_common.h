@@ -28,8 +28,9 @@ constexpr int kWaveQ = 32;                    // queries per wave
 static_assert(kWaves * kWaveQ == kQTile, "query tile must match the plan");
 
 // Softmax reference (log2 units). p = exp2(c*s - ref) is computed against the running
-// reference first; only when a lane's partial tile sum leaves [0, kSumLimit] (a logit
-// about 8 or more above the reference, or the first unmasked tile) is the reference
+// reference first; only when a lane's partial sum of the tile's bf16 weights leaves
+// [0, kSumLimit] (a logit about 8 or more above the reference, or the first unmasked
+// tile) is the reference
 // raised to the tile maximum, O and the row sum rescaled and the tile recomputed. So
 // the per-tile maximum is never needed on the common path. The result is exact:
 // numerator and denominator share the reference. Raising the reference to a new
@@ -218,10 +219,12 @@ __device__ inline void load_q(const uint16_t* qp, bool ok, bf16x8 (&qf)[Cfg<D>::
 }
 
 // p = exp2(c*s - ref) of this lane's 32 scores, packed to bf16 in the P^T operand
-// order; returns the lane's partial sum of the float32 values.
+// order; returns the lane's partial sum of the float32 values when SUM (else 0: a
+// caller that wants no log-sum-exp needs only the bf16 weights).
+template <bool SUM>
 __device__ inline float exp_tile(const f32x16 (&s)[2], float ref, float c_log2, bf16x8 (&pf)[4]) {
   // Two chains, each started from its first pair (p >= 0, so this equals 0 + pair).
-  float sum0, sum1;
+  float sum0 = 0.f, sum1 = 0.f;
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
     const int kb = kc >> 1, half = kc & 1;
@@ -230,9 +233,11 @@ __device__ inline float exp_tile(const f32x16 (&s)[2], float ref, float c_log2, 
       const int r = half * 8 + 2 * e2;
       f32x2 two = {__builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -ref)),
                    __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c_log2, -ref))};
-      const float pr = two[0] + two[1];
-      if (kc & 1) sum1 = (kc == 1 && e2 == 0) ? pr : sum1 + pr;
-      else sum0 = (kc == 0 && e2 == 0) ? pr : sum0 + pr;
+      if (SUM) {
+        const float pr = two[0] + two[1];
+        if (kc & 1) sum1 = (kc == 1 && e2 == 0) ? pr : sum1 + pr;
+        else sum0 = (kc == 0 && e2 == 0) ? pr : sum0 + pr;
+      }
       const bf16x2 cv = __builtin_convertvector(two, bf16x2);
       pf[kc][2 * e2] = cv[0];
       pf[kc][2 * e2 + 1] = cv[1];
@@ -291,8 +296,12 @@ struct KHead {
 // fragments on entry; when ks_next is not null it holds the next tile's on return
 // (read during the second half of P V). LDS fragments are read in batches ahead of
 // their products (the rest of K first; V^T in two halves), so each batch is in flight
-// while earlier work runs.
-template <int D>
+// while earlier work runs. LSE: also sum the float32 weights for the log-sum-exp (30
+// VALU instructions per tile) and check the reference against that sum; without it the
+// check uses the sum of the bf16 weights that O's normaliser needs anyway. The two sums
+// differ by the bf16 rounding, so near the limit the variants may raise the reference
+// at different tiles; O then differs in rounding only.
+template <int D, bool LSE>
 __device__ inline void attend_tile(KHead<D>& kh, const char* ks, const char* ks_next,
                                    const bf16x8 (&qf)[Cfg<D>::DK], Flash<D>& f, bool masked,
                                    int lim, float c_log2) {
@@ -341,8 +350,10 @@ __device__ inline void attend_tile(KHead<D>& kh, const char* ks, const char* ks_
       }
   }
   bf16x8 pf[4];
-  float ps = exp_tile(s, f.mrun, c_log2, pf);
-  if (__any(!(ps <= kSumLimit))) {
+  float ps = exp_tile<LSE>(s, f.mrun, c_log2, pf);
+  float pb = 0.f;
+  if (!LSE) pb = bf16_tile_sum(pf);
+  if (__any(!((LSE ? ps : pb) <= kSumLimit))) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -358,10 +369,14 @@ __device__ inline void attend_tile(KHead<D>& kh, const char* ks, const char* ks_
     for (int dm = 0; dm < C::DM; ++dm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) f.o[dm][r] *= alpha;
-    ps = exp_tile(s, mnew, c_log2, pf);
+    ps = exp_tile<LSE>(s, mnew, c_log2, pf);
+    if (!LSE) pb = bf16_tile_sum(pf);
   }
-  f.lsum += ps;
-  f.lsum_b += bf16_tile_sum(pf);
+  if (LSE) {
+    f.lsum += ps;
+    pb = bf16_tile_sum(pf);
+  }
+  f.lsum_b += pb;
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
 #pragma unroll

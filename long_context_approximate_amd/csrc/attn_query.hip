@@ -120,8 +120,9 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
       int64_t lim = nkeys - key0 - 1;
       if (self && qi - key0 < lim) lim = qi - key0;
       const int lim32 = lim < BN - 1 ? static_cast<int>(lim) : BN - 1;
-      attend_tile<D>(kh, smem + st * C::STAGE, it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr,
-                     qf, f, __any(lim32 < BN - 1) != 0, lim32, c_log2);
+      attend_tile<D, true>(kh, smem + st * C::STAGE,
+                           it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr, qf, f,
+                           __any(lim32 < BN - 1) != 0, lim32, c_log2);
     }
     wait_tile_loads();   // tile it+2
     __syncthreads();

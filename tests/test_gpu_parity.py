@@ -108,6 +108,32 @@ def test_small_full_parity(cfg):
     _check_full(cfg, got, ref)
 
 
+BF16_SMALL = [c for c in SMALL if c.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("cfg", BF16_SMALL, ids=[c.name for c in BF16_SMALL])
+def test_output_without_the_log_sum_exp(cfg):
+    # lse_out = NULL runs the kernel variant without the float32 weight sum; its
+    # reference check uses the bf16 weight sum, so O may differ from the LSE run in
+    # rounding only (a reference raised at another tile). Both must meet the bar.
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    got, x = _gpu_run(cfg)
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    idx = torch.from_numpy(got["idx"]).cuda()
+    out = torch.full((cfg.seq_len, cfg.num_q_heads, cfg.head_dim), float("nan"),
+                     dtype=dev["q"].dtype, device="cuda")
+    spava.spava_approx_attn_fwd(shape, dev["q"], dev["k"], dev["v"], idx, out, None)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    err = np.abs(o - ref["o"]).max()
+    assert err <= TOL["bf16"][0], f"max |dO| = {err:.3e}"
+    print(f"PARITY no-lse {cfg.name}: max|dO| {err:.3e}, max|O - O(lse run)| "
+          f"{np.abs(o - got['out']).max():.3e}", flush=True)
+
+
 def test_attention_with_oracle_indices():
     # Feeds the oracle's own selection to the attention call (decoupled from selection).
     cfg = small_config(name="decoupled", seq_len=2304, num_hosts=3, seed=21)
@@ -599,6 +625,37 @@ def test_overlap_layer_full_size_whole_tiles():
     assert worst_o <= 2e-2, f"max |dO| = {worst_o:.3e}"
     assert worst_l <= 1e-3, f"max |dLSE| = {worst_l:.3e}"
     assert np.isfinite(got["out"]).all() and np.isfinite(got["lse"]).all()
+
+
+@pytest.mark.parametrize("name", ["h4_16k", "t3_h16_256k"])
+def test_output_without_the_log_sum_exp_full_size(name):
+    # The kernel variant without the float32 weight sum (lse_out = NULL) at full size,
+    # the heavy-tailed 256K workload included (its reference is raised most often):
+    # whole query tiles of every third head against the oracle, and the whole output
+    # against the run that writes the LSE.
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    cfg = CONFIGS[name]
+    got, x = _gpu_run(cfg)
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    out = torch.full((cfg.seq_len, cfg.num_q_heads, cfg.head_dim), float("nan"),
+                     dtype=dev["q"].dtype, device="cuda")
+    spava.spava_approx_attn_fwd(shape, dev["q"], dev["k"], dev["v"],
+                                torch.from_numpy(got["idx"]).cuda(), out, None)
+    torch.cuda.synchronize()
+    nolse = {"out": out.float().cpu().numpy(), "lse": got["lse"]}
+    del dev, out
+    vs_lse = float(np.abs(nolse["out"] - got["out"]).max())
+    sh = oracle.shape_of(cfg)
+    rows = _whole_tiles(cfg, np.random.default_rng(cfg.seed + 2))
+    worst_o, _, n = _compare_rows(cfg, sh, x, got["idx"], nolse, rows,
+                                  heads=range(0, cfg.num_q_heads, 3))
+    print(f"PARITY no-lse {cfg.name}: whole tiles, {n} (row, head) outputs; "
+          f"max|dO| = {worst_o:.3e}; max|O - O(lse run)| over all rows = {vs_lse:.3e}")
+    assert worst_o <= 2e-2, f"max |dO| = {worst_o:.3e}"
+    assert vs_lse <= 2e-2, f"max |O - O(lse run)| = {vs_lse:.3e}"
+    assert np.isfinite(nolse["out"]).all()
 
 
 # ------------------------------------------------------------- query block B_qr
