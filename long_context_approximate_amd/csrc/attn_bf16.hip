@@ -252,17 +252,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     // O accumulators in place across iterations.
     const bool diag = it >= it_diag;
     const bool masked = diag || it == it_edge || !wave_active;
-    int lim = BN - 1;
-    if (masked) {
+    auto lim_of = [&]() {
+      int lim = BN - 1;
       if (it == it_edge) lim = L - it * BN - 1;
       if (diag) {
         const int rel = qrel - (it - np) * BN;      // integer select (no floating max)
         lim = rel < 0 ? -1 : rel;
       }
-      if (!wave_active) lim = -1;
-    }
+      return wave_active ? lim : -1;
+    };
     attend_tile<D, LSE>(kh, smem + st * C::STAGE,
-                        it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr, qf, f, masked, lim,
+                        it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr, qf, f, masked, lim_of,
                         c_log2);
     wait_tile_loads();   // tile it+2, which the next iteration's P V reads K from
     __syncthreads();

@@ -290,8 +290,9 @@ struct KHead {
 };
 
 // One 64-key tile (K rows at ks, V^T at ks + KBYTES) for this wave's 32 queries:
-// S^T = K Q^T, then, when `masked` (a wave-uniform flag), hide keys kk > lim (kk = key
-// index inside the tile; lim >= 63 hides nothing), online softmax in the log2 domain
+// S^T = K Q^T, then, when `masked` (a wave-uniform flag), hide keys kk > lim() (kk = key
+// index inside the tile; lim() >= 63 hides nothing; evaluated only for masked tiles, so
+// unmasked ones pay no per-lane limit arithmetic), online softmax in the log2 domain
 // against the running reference, then O^T += V^T P^T. kh holds this tile's first K
 // fragments on entry; when ks_next is not null it holds the next tile's on return
 // (read during the second half of P V). LDS fragments are read in batches ahead of
@@ -301,10 +302,10 @@ struct KHead {
 // check uses the sum of the bf16 weights that O's normaliser needs anyway. The two sums
 // differ by the bf16 rounding, so near the limit the variants may raise the reference
 // at different tiles; O then differs in rounding only.
-template <int D, bool LSE>
+template <int D, bool LSE, typename LimFn>
 __device__ inline void attend_tile(KHead<D>& kh, const char* ks, const char* ks_next,
                                    const bf16x8 (&qf)[Cfg<D>::DK], Flash<D>& f, bool masked,
-                                   int lim, float c_log2) {
+                                   LimFn lim_of, float c_log2) {
   using C = Cfg<D>;
   constexpr int KH = KHead<D>::kSteps;
   const int lane = threadIdx.x & 63;
@@ -341,6 +342,7 @@ __device__ inline void attend_tile(KHead<D>& kh, const char* ks, const char* ks_
   read_v(1);
   __builtin_amdgcn_sched_barrier(0);
   if (masked) {
+    const int lim = lim_of();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

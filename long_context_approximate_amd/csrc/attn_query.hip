@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
       const int lim32 = lim < BN - 1 ? static_cast<int>(lim) : BN - 1;
       attend_tile<D, true>(kh, smem + st * C::STAGE,
                            it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr, qf, f,
-                           __any(lim32 < BN - 1) != 0, lim32, c_log2);
+                           __any(lim32 < BN - 1) != 0, [=]() { return lim32; }, c_log2);
     }
     wait_tile_loads();   // tile it+2
     __syncthreads();
