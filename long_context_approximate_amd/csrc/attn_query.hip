@@ -12,8 +12,8 @@
 //   vt_rows    V^T tiles (MFMA slot order) of the context blocks and of the query keys;
 //   partial    bf16: one workgroup = 256 query rows x 1 head x 1 partial (H context
 //              blocks + the query block itself), the same flash step as the main
-//              attention; f32: each query row on a lane pair, float64 arithmetic
-//              except the float32 exponentials;
+//              attention; f32: 64 query rows per workgroup on the float64 matrix
+//              cores, the main float32 attention's step (float32 exponentials);
 //   merge      O = sum_h exp(LSE_h - LSE) O_h with LSE = log sum_h exp(LSE_h).
 #include "attn_common.h"
 #include "attn_f32_step.h"
@@ -147,44 +147,44 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
   }
 }
 
-// float32 inputs: each query row on a lane pair (see F32Row); grid
-// ((H + 1) * ceil(nq / 64), Hq), two waves of 32 rows.
+// float32 inputs on the float64 matrix cores (F64Flash); grid
+// ((H + 1) * ceil(nq / 64), Hq), four waves of 16 rows.
 template <int D>
-__global__ __launch_bounds__(128) void query_partial_f32_kernel(
+__global__ __launch_bounds__(256, 2) void query_partial_f32_kernel(
     Plan p, int64_t nq, int qtiles, const float* __restrict__ q_qr, const float* __restrict__ k_qr,
     const float* __restrict__ v_qr, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ part_o, double* __restrict__ part_lse) {
-  __shared__ F32Tile<D> tile;
+  __shared__ __attribute__((aligned(16))) F64Tile<D> tile;
   const int ph = blockIdx.x / qtiles, qt = blockIdx.x % qtiles;
   const int hq = blockIdx.y, g = hq / p.G;
   const bool self = ph == p.H;
-  const int tid = threadIdx.x;
-  const int64_t qi = static_cast<int64_t>(qt) * BN + (tid >> 6) * 32 + (tid & 31);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t qi = static_cast<int64_t>(qt) * kF64QTile + w * 16 + (lane & 15);
   const bool valid = qi < nq;
-  const int64_t q_last = min(static_cast<int64_t>(qt + 1) * BN, nq) - 1;
+  const int64_t q_last = min(static_cast<int64_t>(qt + 1) * kF64QTile, nq) - 1;
   const float* kb = self ? k_qr : k + static_cast<int64_t>(ph) * p.nb * p.kvs_tok;
   const float* vb = self ? v_qr : v + static_cast<int64_t>(ph) * p.nb * p.kvs_tok;
   const int64_t nkeys = self ? q_last + 1 : p.nb;
 
-  F32Row<D> row;
-  row.init(valid ? q_qr + qi * p.qs_tok + hq * p.qs_head : nullptr);
+  F64Flash<D> f;
+  f.init(valid ? q_qr + qi * p.qs_tok + hq * p.qs_head : nullptr);
   for (int64_t key0 = 0; key0 < nkeys; key0 += BN) {
     __syncthreads();
-    f32_load_tile<D>(
-        tile, static_cast<int>(min<int64_t>(BN, nkeys - key0)),
-        [&](int r) { return kb + (key0 + r) * p.kvs_tok + g * p.kvs_head; },
-        [&](int r) { return vb + (key0 + r) * p.kvs_tok + g * p.kvs_head; }, 128);
+    f64_load_tile<D>(tile, kb + key0 * p.kvs_tok + g * p.kvs_head,
+                     vb + key0 * p.kvs_tok + g * p.kvs_head, p.kvs_tok,
+                     static_cast<int>(min<int64_t>(BN, nkeys - key0)));
     __syncthreads();
     // Visible keys form a prefix of the tile: all present keys of a context block, the
     // query keys up to the row itself.
     int64_t lim = nkeys - 1 - key0;
     if (self) lim = min(lim, qi - key0);
-    row.step(tile, valid ? static_cast<int>(min<int64_t>(lim, BN - 1)) : -1, p.scale);
+    f.step(tile, valid ? static_cast<int>(min<int64_t>(lim, BN - 1)) : -1, p.scale);
   }
+  f.finish();
   if (!valid) return;
-  row.store(part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * D);
+  f.store(part_o + ((static_cast<int64_t>(ph) * nq + qi) * p.Hq + hq) * D);
   // The partial's LSE is kept in float64 for the merge weights exp(LSE_h - LSE).
-  if (row.half == 0) part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] = row.lse();
+  if ((lane >> 4) == 0) part_lse[(static_cast<int64_t>(ph) * p.Hq + hq) * nq + qi] = f.lse();
 }
 
 __device__ inline void store4(uint16_t* dst, float4 v) {
@@ -268,9 +268,9 @@ hipError_t launch_query_f32(const Plan& p, int64_t nq, const float* q_qr, const 
   const QueryWs w = query_ws_layout(p, nq);
   float* part_o = reinterpret_cast<float*>(ws + w.part_o);
   double* part_lse = reinterpret_cast<double*>(ws + w.part_lse);
-  const int qtiles = static_cast<int>(cdiv(nq, BN));
+  const int qtiles = static_cast<int>(cdiv(nq, kF64QTile));
   hipLaunchKernelGGL(query_partial_f32_kernel<D>,
-                     dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq), dim3(128), 0, st, p,
+                     dim3(static_cast<unsigned>((p.H + 1) * qtiles), p.Hq), dim3(256), 0, st, p,
                      nq, qtiles, q_qr, k_qr, v_qr, k, v, part_o, part_lse);
   const int64_t threads = nq * p.Hq * (p.D / 4);
   const dim3 mgrid(static_cast<unsigned>(cdiv(threads, 256)));
