@@ -177,24 +177,26 @@ def test_duplicated_keys_tie_to_lower_position():
     _check_full(cfg, got, ref)
 
 
-def test_strided_layout():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_layout(dtype):
     # q/out live inside wider [N, Hq, 2d] buffers; k/v inside [N, 2*Hkv, d] buffers.
     torch = _torch()
-    cfg = small_config(name="strided", seq_len=1200, num_hosts=2, seed=24)
+    cfg = small_config(name=f"strided_{dtype}", seq_len=1200, num_hosts=2, dtype=dtype, seed=24)
     n, hq, hkv, d = cfg.seq_len, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     holder = {}
 
     def make(dev):
-        qw = torch.zeros((n, hq, 2 * d), dtype=torch.bfloat16, device="cuda")
+        qw = torch.zeros((n, hq, 2 * d), dtype=tdt, device="cuda")
         qw[:, :, :d] = dev["q"]
-        kw = torch.zeros((n, 2 * hkv, d), dtype=torch.bfloat16, device="cuda")
-        vw = torch.zeros((n, 2 * hkv, d), dtype=torch.bfloat16, device="cuda")
+        kw = torch.zeros((n, 2 * hkv, d), dtype=tdt, device="cuda")
+        vw = torch.zeros((n, 2 * hkv, d), dtype=tdt, device="cuda")
         kw[:, :hkv] = dev["k"]
         vw[:, :hkv] = dev["v"]
         return {"q": qw[:, :, :d], "k": kw[:, :hkv], "v": vw[:, :hkv]}
 
     def out():
-        holder["o"] = torch.zeros((n, hq, 2 * d), dtype=torch.bfloat16, device="cuda")
+        holder["o"] = torch.zeros((n, hq, 2 * d), dtype=tdt, device="cuda")
         return holder["o"][:, :, :d]
 
     strides = {"shape": (hq * 2 * d, 2 * d, 2 * hkv * d, d, hq * 2 * d, 2 * d), "make": make,
