@@ -235,6 +235,16 @@ def test_random_shapes(seed):
     _check_full(cfg, got, ref)
 
 
+@pytest.mark.parametrize("seed", range(32, 48))
+def test_random_shapes_f32(seed):
+    # The same random shapes with float32 inputs (the float64 matrix-core path).
+    cfg = _random_config(seed).with_(dtype="f32")
+    got, x = _gpu_run(cfg)
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    _check_selection(cfg, got, ref)
+    _check_full(cfg, got, ref)
+
+
 def test_large_kv_token_stride():
     # k/v rows 64K elements (128 KB) apart: the tile loads address K rows in place through
     # 32-bit buffer offsets of up to 63 token strides, and clip the ragged last tile.
