@@ -566,7 +566,7 @@ def test_layer_on_a_side_stream_while_the_current_stream_allocates():
 
 # ------------------------- overlapped layer (selection beside block 0's attention)
 
-def _gpu_overlap(cfg, x):
+def _gpu_overlap(cfg, x, with_lse=True):
     torch = _torch()
     from long_context_approximate_amd import spava
     dev = spava.device_tensors(x, "cuda")
@@ -579,8 +579,8 @@ def _gpu_overlap(cfg, x):
     lse = torch.full((cfg.num_q_heads, cfg.seq_len), float("nan"), dtype=torch.float32,
                      device="cuda")
     side = torch.cuda.Stream()
-    spava.spava_layer_overlap_fwd(shape, dev["q"], dev["k"], dev["v"], idx, out, lse, scores,
-                                  side_stream=side)
+    spava.spava_layer_overlap_fwd(shape, dev["q"], dev["k"], dev["v"], idx, out,
+                                  lse if with_lse else None, scores, side_stream=side)
     torch.cuda.synchronize()
     return {"idx": idx.cpu().numpy(), "scores": scores.cpu().numpy(),
             "out": out.float().cpu().numpy(), "lse": lse.cpu().numpy()}
@@ -616,6 +616,29 @@ def test_overlap_layer_parity(cfg):
     _check_full(cfg, got, ref)
     two, _ = _gpu_run(cfg, x)
     _assert_same_as_two_calls(got, two)
+
+
+@pytest.mark.parametrize("cfg", OVERLAP[:3], ids=[c.name for c in OVERLAP[:3]])
+def test_overlap_layer_without_the_log_sum_exp(cfg):
+    # lse_out = NULL: both of the overlapped layer's attention launches take the kernel
+    # variant without the float32 weight sum; O must be that of the two calls with
+    # lse_out = NULL, bitwise, and the LSE buffer must stay untouched.
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    x = make_inputs(cfg)
+    got = _gpu_overlap(cfg, x, with_lse=False)
+    assert np.isnan(got["lse"]).all()
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    out = torch.full((cfg.seq_len, cfg.num_q_heads, cfg.head_dim), float("nan"),
+                     dtype=dev["q"].dtype, device="cuda")
+    spava.spava_approx_attn_fwd(shape, dev["q"], dev["k"], dev["v"],
+                                torch.from_numpy(got["idx"]).cuda(), out, None)
+    torch.cuda.synchronize()
+    two = out.float().cpu().numpy()
+    assert np.array_equal(got["out"].view(np.uint8), two.view(np.uint8))
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"])
+    assert np.abs(got["out"] - ref["o"]).max() <= TOL["bf16"][0]
 
 
 def test_overlap_layer_full_size_whole_tiles():
