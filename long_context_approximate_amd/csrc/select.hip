@@ -227,9 +227,12 @@ __device__ inline int64_t logit_at(const Plan& p, int r, int64_t kk) {   // kk =
 
 // One wave per (jg, 32-row tile, key split) for the pairs [jg0, jg0 + npairs). Waves
 // are independent (no barriers). STORE: also write the scaled logits of every visible
-// (row, key) to the stored-logit layout above.
-template <typename T, int D, bool STORE>
-__global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restrict__ q,
+// (row, key) to the stored-logit layout above. MINB = 2 caps the registers at two waves
+// per SIMD (a few spills), for launches with more waves than SIMDs: the second wave
+// hides the first's memory and dependency stalls (the float64 products and the
+// vector work of a SIMD do not overlap, so a wave alone leaves the stalls exposed).
+template <typename T, int D, bool STORE, int MINB>
+__global__ __launch_bounds__(256, MINB) void rowstats_kernel(Plan p, const T* __restrict__ q,
                                                        const T* __restrict__ k,
                                                        double2* __restrict__ part,
                                                        double* __restrict__ logits,
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
   Frag<T, D> qa[2];
   load_rows<T, D>(p, q, j, g, r0, col, kg, qa);
   double m[2][4], z[2][4];
-  int64_t qi[2][4];
+  int qi[2][4];   // last visible key of each row, relative to s (-1: padding row)
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -262,11 +265,12 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
       m[rb][rr] = -INFINITY;
       z[rb][rr] = 0.0;
       const int r = r0 + rb * 16 + 4 * rr + kg;
-      qi[rb][rr] = r < p.R ? row_key_limit(p, j, r) : -1;   // -1: padding row sees nothing
+      qi[rb][rr] =
+          r < p.R ? static_cast<int>(min<int64_t>(row_key_limit(p, j, r) - s, p.nb)) : -1;
     }
   // Last key every row of this wave sees (wave-uniform); tiles at or below it, inside
   // the split and without padding rows take the unmasked path.
-  int64_t qmin = INT64_MAX;
+  int qmin = INT32_MAX;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
     // Prefetch the next key tile while this tile's softmax statistics are formed.
     if (key0 + kWaveKeys < split_hi)
       load_keys<T, D>(p, k, g, key0 + kWaveKeys, split_hi, col, kg, kf);
-    const bool full = rows_full && key0 + kWaveKeys <= split_hi && key0 + kWaveKeys - 1 <= qmin;
+    const bool full = rows_full && key0 + kWaveKeys <= split_hi && key0 + kWaveKeys - 1 <= s + qmin;
     if (full) {
       // Every (row, key) of the tile is visible: the same updates without masks.
 #pragma unroll
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(Plan p, const T* __restri
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int64_t key = key0 + kb * 16 + col;
-          vis[kb] = key < split_hi && key <= qi[rb][rr];
+          vis[kb] = key < split_hi && key - s <= qi[rb][rr];
           x[kb] = p.scale * acc[rb][kb][rr];
           if (vis[kb]) mt = fmax(mt, x[kb]);
           if (STORE && vis[kb])
@@ -654,6 +658,15 @@ __global__ __launch_bounds__(1024) void topl_kernel(Plan p, const double* __rest
 
 }  // namespace
 
+// Row statistics at two waves per SIMD: bf16 inputs, launches with more waves than
+// SIMDs. float32 fragments take twice the registers (hundreds of spills at that cap).
+template <typename T>
+constexpr int kTwoWaves = sizeof(T) == 2 ? 2 : 1;
+template <typename T>
+static bool two_waves_per_simd(int64_t waves) {
+  return sizeof(T) == 2 && waves > kScoreWaveSlots;
+}
+
 template <typename T, int D>
 static hipError_t launch_select_t(const Plan& p, const T* q, const T* k, int32_t* idx,
                                   double* scores_out, char* ws, hipStream_t st) {
@@ -669,8 +682,13 @@ static hipError_t launch_select_t(const Plan& p, const T* q, const T* k, int32_t
     for (int jg0 = 0; jg0 < JG; jg0 += p.pair_chunk) {
       const int np = std::min(p.pair_chunk, JG - jg0);
       const int64_t w1 = static_cast<int64_t>(np) * row_tiles * p.KS;
-      hipLaunchKernelGGL((rowstats_kernel<T, D, true>), dim3(static_cast<unsigned>(cdiv(w1, 4))),
-                         dim3(256), 0, st, p, q, k, part, logits, row_tiles, jg0, np);
+      const dim3 grid(static_cast<unsigned>(cdiv(w1, 4)));
+      if (two_waves_per_simd<T>(w1))
+        hipLaunchKernelGGL((rowstats_kernel<T, D, true, kTwoWaves<T>>), grid, dim3(256), 0, st, p, q, k, part,
+                           logits, row_tiles, jg0, np);
+      else
+        hipLaunchKernelGGL((rowstats_kernel<T, D, true, 1>), grid, dim3(256), 0, st, p, q, k, part,
+                           logits, row_tiles, jg0, np);
       const int64_t rows = static_cast<int64_t>(np) * p.R;
       hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(cdiv(rows, 256))), dim3(256), 0,
                          st, p, part, rowstat, jg0, np);
@@ -680,8 +698,13 @@ static hipError_t launch_select_t(const Plan& p, const T* q, const T* k, int32_t
     }
   } else {
     const int64_t w1 = static_cast<int64_t>(JG) * row_tiles * p.KS;
-    hipLaunchKernelGGL((rowstats_kernel<T, D, false>), dim3(static_cast<unsigned>(cdiv(w1, 4))),
-                       dim3(256), 0, st, p, q, k, part, nullptr, row_tiles, 0, JG);
+    const dim3 grid(static_cast<unsigned>(cdiv(w1, 4)));
+    if (two_waves_per_simd<T>(w1))
+      hipLaunchKernelGGL((rowstats_kernel<T, D, false, kTwoWaves<T>>), grid, dim3(256), 0, st, p, q, k, part,
+                         nullptr, row_tiles, 0, JG);
+    else
+      hipLaunchKernelGGL((rowstats_kernel<T, D, false, 1>), grid, dim3(256), 0, st, p, q, k, part,
+                         nullptr, row_tiles, 0, JG);
     const int64_t rows = static_cast<int64_t>(JG) * p.R;
     hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(cdiv(rows, 256))), dim3(256), 0, st,
                        p, part, rowstat, 0, JG);
