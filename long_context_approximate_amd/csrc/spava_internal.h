@@ -15,7 +15,9 @@ constexpr int kQTile = 256;      // queries per attention workgroup (8 waves x 3
 // the pass takes about ceil(waves / kScoreWaveSlots) * (split + kScoreWaveOverhead)
 // key steps, kScoreWaveSlots = 256 CUs x 4 SIMDs (a fit to timings of split lengths
 // 512..2048 at 16384 keys per block). The split length, a multiple of 32 in
-// [kScoreSplitMin, kScoreSplitMax], minimises that estimate (ties: the longer).
+// [kScoreSplitMin, kScoreSplitMax], minimises that estimate (ties: the longer). A
+// launch with more waves than kScoreWaveSlots (bf16) uses the build capped at two waves
+// per SIMD.
 constexpr int kScoreSplitMin = 512;
 constexpr int kScoreSplitMax = 4096;
 constexpr int kScoreWaveSlots = 1024;
