@@ -245,6 +245,50 @@ def test_random_shapes_f32(seed):
     _check_full(cfg, got, ref)
 
 
+# Selection launches with more row-statistics waves than the chip has SIMDs take the
+# build capped at two waves per SIMD; these shapes reach it with ragged observer counts
+# (R = G * w not a multiple of 32) and ragged blocks. The wave count follows the split
+# rule (a multiple of 32 in [512, 4096] minimising ceil(waves / 1024) * (split + 32)).
+TWO_WAVE_SELECT = [
+    small_config(name="sel_2w_normal", seq_len=4 * 5000, num_hosts=4, num_q_heads=28,
+                 num_kv_heads=4, anchor_len=256, passing_len=300, window=100, seed=41),
+    small_config(name="sel_2w_t3", seq_len=5 * 4010, num_hosts=5, num_q_heads=28,
+                 num_kv_heads=4, anchor_len=64, passing_len=777, window=97,
+                 dist="student_t3", seed=42),
+]
+
+
+def _score_waves(cfg):
+    jg = (cfg.num_hosts - 1) * cfg.num_kv_heads
+    R = (cfg.num_q_heads // cfg.num_kv_heads) * cfg.window
+    nb = cfg.seq_len // cfg.num_hosts
+    units = jg * -(-R // 32)
+    best = None
+    for split in range(4096, 511, -32):
+        cost = -(-units * -(-nb // split) // 1024) * (min(split, nb) + 32)
+        if best is None or cost < best[0]:
+            best = (cost, split)
+    return units * -(-nb // best[1])
+
+
+@pytest.mark.parametrize("cfg", TWO_WAVE_SELECT, ids=[c.name for c in TWO_WAVE_SELECT])
+def test_selection_two_waves_per_simd(cfg):
+    assert _score_waves(cfg) > 1024
+    torch = _torch()
+    from long_context_approximate_amd import spava
+    x = make_inputs(cfg)
+    dev = spava.device_tensors(x, "cuda")
+    shape = spava.shape_from_config(cfg)
+    H, hkv, l, nb = cfg.num_hosts, cfg.num_kv_heads, cfg.passing_len, cfg.block_len
+    idx = torch.full((H - 1, hkv, l), -7, dtype=torch.int32, device="cuda")
+    scores = torch.full((H - 1, hkv, nb), -1.0, dtype=torch.float64, device="cuda")
+    spava.spava_select_passing(shape, dev["q"], dev["k"], idx, scores)
+    torch.cuda.synchronize()
+    got = {"idx": idx.cpu().numpy(), "scores": scores.cpu().numpy()}
+    ref = oracle.run(oracle.shape_of(cfg), x["q"], x["k"], x["v"], attention=False)
+    _check_selection(cfg, got, ref)
+
+
 def test_large_kv_token_stride():
     # k/v rows 64K elements (128 KB) apart: the tile loads address K rows in place through
     # 32-bit buffer offsets of up to 63 token strides, and clip the ragged last tile.
