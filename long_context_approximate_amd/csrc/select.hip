@@ -173,7 +173,10 @@ __device__ inline void init_exp_table(double* tab) {
   if (threadIdx.x < kExpTab) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) / kExpTab);
   __syncthreads();
 }
-__device__ inline double exp_tab(double y, const double* tab) {
+// The routine without its final underflow select: below -745.2 it returns 0 or a
+// subnormal (at most 2^-1074) instead of 0. The row sums use it: a sum that already
+// holds a term of at least 1 (the reference's own) is bitwise unchanged by that.
+__device__ inline double exp_tab_raw(double y, const double* tab) {
   const double yc = fmax(y, -746.0);
   const double k = rint(yc * 0x1.71547652b82fep+6);         // y * 64 / ln2
   double r = fma(-k, 0x1.62e42fefa0000p-7, yc);             // head of ln2 / 64
@@ -184,7 +187,11 @@ __device__ inline double exp_tab(double y, const double* tab) {
   a = fma(r, a, 1.0);
   const double er = fma(r, a, 1.0);
   const int ki = static_cast<int>(k);
-  const double v = ldexp(tab[ki & (kExpTab - 1)] * er, ki >> 6);
+  return ldexp(tab[ki & (kExpTab - 1)] * er, ki >> 6);
+}
+__device__ inline double exp_tab(double y, const double* tab) {
+  const double yc = fmax(y, -746.0);
+  const double v = exp_tab_raw(yc, tab);
   return yc > -745.2 ? v : 0.0;
 }
 
@@ -291,15 +298,16 @@ __global__ __launch_bounds__(256, MINB) void rowstats_kernel(Plan p, const T* __
     const bool full = rows_full && key0 + kWaveKeys <= split_hi && key0 + kWaveKeys - 1 <= s + qmin;
     if (full) {
       // Every (row, key) of the tile is visible: the same updates without masks.
+      double* tb = STORE ? lg + logit_at(p, r0 + kg, key0 - s) + col : nullptr;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const double x0 = p.scale * acc[rb][0][rr], x1 = p.scale * acc[rb][1][rr];
           if (STORE) {
-            double* row = lg + logit_at(p, r0 + rb * 16 + 4 * rr + kg, key0 - s);   // slot 0
-            __builtin_nontemporal_store(x0, row + col);
-            __builtin_nontemporal_store(x1, row + 16 + col);
+            double* row = tb + (rb * 16 + 4 * rr) * 32;   // rows of one tile are 32 apart
+            __builtin_nontemporal_store(x0, row);
+            __builtin_nontemporal_store(x1, row + 16);
           }
           const double mt = fmax(x0, x1);
           if (mt > m[rb][rr] + kRefMargin) {
@@ -307,8 +315,8 @@ __global__ __launch_bounds__(256, MINB) void rowstats_kernel(Plan p, const T* __
                 (m[rb][rr] == -INFINITY) ? 0.0 : z[rb][rr] * exp_tab(m[rb][rr] - mt, etab);
             m[rb][rr] = mt;
           }
-          z[rb][rr] += exp_tab(x0 - m[rb][rr], etab);
-          z[rb][rr] += exp_tab(x1 - m[rb][rr], etab);
+          z[rb][rr] += exp_tab_raw(x0 - m[rb][rr], etab);
+          z[rb][rr] += exp_tab_raw(x1 - m[rb][rr], etab);
         }
       continue;
     }
