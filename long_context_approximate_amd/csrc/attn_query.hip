@@ -69,11 +69,10 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
   const int ph = (gs / p.Hkv) / qtiles, qt = (gs / p.Hkv) % qtiles;
   const bool self = ph == p.H;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t q0 = static_cast<int64_t>(qt) * kQTile;
   const int64_t qw0 = q0 + static_cast<int64_t>(kWaveQ) * w;
-  const int64_t qw_last = qw0 + kWaveQ - 1;
   const int64_t qi = qw0 + lr;
   const bool wave_active = qw0 < nq;
 
@@ -101,32 +100,44 @@ __global__ __launch_bounds__(kThreads) void query_partial_kernel(
 
   // The main attention's three-stage ring: while tile it is computed, tile it+1 is
   // complete (its first K fragments are read during tile it's P V) and tile it+2 is in
-  // flight. A wave that skips a tile (past its queries in the query block, or no
-  // queries at all) skips every later one, so it never needs the prefetched fragments.
+  // flight.
   if (ntiles > 0) issue_tile(0, smem);
   if (ntiles > 1) issue_tile(1, smem + C::STAGE);
   wait_tile_loads();
   __syncthreads();
-  KHead<D> kh;
-  if (ntiles > 0) kh.read(smem);
   int st = 0;   // stage of tile it
-  for (int it = 0; it < ntiles; ++it) {
-    const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
-    if (it + 2 < ntiles) issue_tile(it + 2, smem + st2 * C::STAGE);
-    const int64_t key0 = static_cast<int64_t>(it) * BN;
-    const bool skip = !wave_active || (self && key0 > qw_last);
-    if (!skip) {
-      // Hide keys past the segment end; in the query block also keys after the query.
+  if (!wave_active) {
+    // No queries in this wave: it only loads its share of every tile. (Decided once,
+    // outside the loop: a branch around the tile step inside it made the compiler copy
+    // the O accumulators and the prefetched K fragments on every tile.)
+    for (int it = 0; it < ntiles; ++it) {
+      const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+      if (it + 2 < ntiles) issue_tile(it + 2, smem + st2 * C::STAGE);
+      wait_tile_loads();
+      __syncthreads();
+      st = st1;
+    }
+  } else {
+    KHead<D> kh;
+    if (ntiles > 0) kh.read(smem);
+    for (int it = 0; it < ntiles; ++it) {
+      const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+      if (it + 2 < ntiles) issue_tile(it + 2, smem + st2 * C::STAGE);
+      const int64_t key0 = static_cast<int64_t>(it) * BN;
+      // Hide keys past the segment end; in the query block also keys after the query
+      // (tiles past all of the wave's queries run fully masked: limit -1, every weight
+      // 0, the state unchanged).
       int64_t lim = nkeys - key0 - 1;
       if (self && qi - key0 < lim) lim = qi - key0;
+      if (lim < -1) lim = -1;
       const int lim32 = lim < BN - 1 ? static_cast<int>(lim) : BN - 1;
       attend_tile<D, true>(kh, smem + st * C::STAGE,
                            it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr, qf, f,
                            __any(lim32 < BN - 1) != 0, [=]() { return lim32; }, c_log2);
+      wait_tile_loads();   // tile it+2
+      __syncthreads();
+      st = st1;
     }
-    wait_tile_loads();   // tile it+2
-    __syncthreads();
-    st = st1;
   }
   const float ltot = flash_rowsum<D>(f);       // float32 weights: the LSE
   const float ltot_b = flash_rowsum_b<D>(f);   // bf16 weights: normalises O
