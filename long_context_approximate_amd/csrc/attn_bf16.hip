@@ -240,31 +240,45 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   if (ntiles > 1) issue_tile(1, smem + C::STAGE);
   wait_tile_loads();
   __syncthreads();
-  KHead<D> kh;
-  kh.read(smem);
+  // Local tiles past this wave's last query are fully masked for it: the wave computes
+  // tiles [0, it_end) and only loads its share of the rest, in a second, load-only loop
+  // (chosen once per wave: a branch around the tile step inside one loop made the
+  // compiler copy the O accumulators on every tile). A wave past the block end only
+  // loads.
+  const int64_t q_last = min(qw0 + kWaveQ, e_h) - 1;
+  const int it_end = wave_active ? min(ntiles, np + static_cast<int>((q_last - s_h) / BN) + 1) : 0;
   int st = 0;   // stage of tile it
-  for (int it = 0; it < ntiles; ++it) {
+  if (it_end > 0) {
+    KHead<D> kh;
+    kh.read(smem);
+    for (int it = 0; it < it_end; ++it) {
+      const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+      if (it + 2 < ntiles) issue_tile(it + 2, smem + st2 * C::STAGE);
+      // Last visible key of a masked tile: the prefix length in the partial prefix
+      // tile, the causal diagonal in a local tile.
+      const bool diag = it >= it_diag;
+      const bool masked = diag || it == it_edge;
+      auto lim_of = [&]() {
+        int lim = BN - 1;
+        if (it == it_edge) lim = L - it * BN - 1;
+        if (diag) {
+          const int rel = qrel - (it - np) * BN;      // integer select (no floating max)
+          lim = rel < 0 ? -1 : rel;
+        }
+        return lim;
+      };
+      attend_tile<D, LSE>(kh, smem + st * C::STAGE,
+                          it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr, qf, f, masked, lim_of,
+                          c_log2);
+      wait_tile_loads();   // tile it+2, which the next iteration's P V reads K from
+      __syncthreads();
+      st = st1;
+    }
+  }
+  for (int it = it_end; it < ntiles; ++it) {
     const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
     if (it + 2 < ntiles) issue_tile(it + 2, smem + st2 * C::STAGE);
-    // Last visible key of a masked tile: the prefix length in the partial prefix
-    // tile, the causal diagonal in a local tile. Tiles past this wave's queries are
-    // processed fully masked (lim = -1) rather than branched around, which keeps the
-    // O accumulators in place across iterations.
-    const bool diag = it >= it_diag;
-    const bool masked = diag || it == it_edge || !wave_active;
-    auto lim_of = [&]() {
-      int lim = BN - 1;
-      if (it == it_edge) lim = L - it * BN - 1;
-      if (diag) {
-        const int rel = qrel - (it - np) * BN;      // integer select (no floating max)
-        lim = rel < 0 ? -1 : rel;
-      }
-      return wave_active ? lim : -1;
-    };
-    attend_tile<D, LSE>(kh, smem + st * C::STAGE,
-                        it + 1 < ntiles ? smem + st1 * C::STAGE : nullptr, qf, f, masked, lim_of,
-                        c_log2);
-    wait_tile_loads();   // tile it+2, which the next iteration's P V reads K from
+    wait_tile_loads();
     __syncthreads();
     st = st1;
   }
