@@ -13,7 +13,8 @@
 //              transposes each block's local V into the same tile format;
 //   schedule   orders the (block, query tile) pairs (longest first by default);
 //   attention  one workgroup = 256 queries x 1 query head = 8 waves x 32 queries
-//              (2 waves per SIMD). K/V tiles of 64 keys are double-buffered in LDS;
+//              (2 waves per SIMD). K/V tiles of 64 keys go through a three-stage
+//              LDS ring, loaded two tiles ahead;
 //              each tile is one flash step (attn_common.h): S^T = K Q^T and
 //              O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with float32 accumulators
 //              and an online softmax in float32 with exp2 and a folded scale.
