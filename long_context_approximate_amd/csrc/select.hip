@@ -94,7 +94,7 @@ struct Frag<float, D> {
 
 // Keep a loop-invariant fragment as stored bits: the empty asm tells the compiler the
 // words may change, so the fp64 widening is redone per use instead of hoisted into
-// 2x as many registers (which would cap occupancy at one wave per SIMD).
+// twice the registers (more than two waves per SIMD can hold).
 template <typename F>
 __device__ inline void opaque(F& f) {
 #pragma unroll
